@@ -1,0 +1,142 @@
+"""ctypes front-end of the CPU oracle for paged-attention decode.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library or its binding.
+All arrays are host numpy arrays; fp16 data is passed as raw 16-bit patterns.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected float16/uint16 data, got {a.dtype}")
+    return a
+
+
+class Oracle:
+    """Handle on one compiled oracle library (the default one, or a variant)."""
+
+    def __init__(self, path=None):
+        path = path or _build.LIB
+        if not os.path.exists(path):
+            _build.build(quiet=True)
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_half_to_double.restype = ctypes.c_double
+        lib.oracle_half_array_to_double.argtypes = [_P, _P, _I64]
+        lib.oracle_half_array_to_double.restype = None
+        lib.oracle_gather.argtypes = [_P, _P, _P, _P, _P, _P] + [_I32] * 7
+        lib.oracle_gather.restype = ctypes.c_int
+        lib.oracle_decode_pairs.argtypes = ([_P, _P, _I32, _P, _P, _P, _P, _P] + [_I32] * 6
+                                            + [ctypes.c_double, _P])
+        lib.oracle_decode_pairs.restype = ctypes.c_int
+        lib.oracle_decode.argtypes = [_P] * 6 + [_I32] * 6 + [ctypes.c_double, _P]
+        lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_reshape_and_cache.argtypes = [_P] * 5 + [_I32] * 5
+        lib.oracle_reshape_and_cache.restype = ctypes.c_int
+        self.lib = lib
+        self.threads_used = 1
+
+    # -- binary16 decoding -------------------------------------------------
+    def half_to_double(self, bits):
+        src = _u16(np.asarray(bits))
+        out = np.empty(src.shape, dtype=np.float64)
+        self.lib.oracle_half_array_to_double(_ptr(src), _ptr(out), src.size)
+        return out
+
+    # -- gather ---------------------------------------------------------------
+    def gather(self, k_cache, v_cache, block_tables, context_lens, seq, head):
+        k_cache, v_cache = _u16(k_cache), _u16(v_cache)
+        nb, bs, nh, hd = k_cache.shape
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        L = int(cl[seq])
+        K = np.empty((max(L, 1), hd), dtype=np.float64)
+        V = np.empty((max(L, 1), hd), dtype=np.float64)
+        rc = self.lib.oracle_gather(_ptr(K), _ptr(V), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
+                                    _ptr(cl), seq, head, nh, hd, nb, bs, bt.shape[1])
+        if rc < 0:
+            raise ValueError(f"oracle_gather failed ({rc})")
+        return K[:L], V[:L]
+
+    # -- decode ---------------------------------------------------------------
+    def decode(self, q, k_cache, v_cache, block_tables, context_lens, scale):
+        """fp64 [S, H, D] attention output for every (sequence, head)."""
+        q, k_cache, v_cache = _u16(q), _u16(k_cache), _u16(v_cache)
+        S, H, D = q.shape
+        nb, bs, nh, hd = k_cache.shape
+        assert (nh, hd) == (H, D) and v_cache.shape == k_cache.shape
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        out = np.empty((S, H, D), dtype=np.float64)
+        used = np.zeros(1, dtype=np.int32)
+        rc = self.lib.oracle_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
+                                    _ptr(cl), S, H, D, nb, bs, bt.shape[1], float(scale),
+                                    _ptr(used))
+        if rc:
+            raise ValueError(f"oracle_decode failed ({rc})")
+        self.threads_used = int(used[0])
+        return out
+
+    def decode_pairs(self, pairs, q, k_cache, v_cache, block_tables, context_lens, scale):
+        """fp64 [len(pairs), D] outputs for the listed (sequence, head) pairs."""
+        q, k_cache, v_cache = _u16(q), _u16(k_cache), _u16(v_cache)
+        S, H, D = q.shape
+        nb, bs, nh, hd = k_cache.shape
+        assert (nh, hd) == (H, D) and v_cache.shape == k_cache.shape
+        pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        out = np.empty((pr.shape[0], D), dtype=np.float64)
+        used = np.zeros(1, dtype=np.int32)
+        rc = self.lib.oracle_decode_pairs(_ptr(out), _ptr(pr), pr.shape[0], _ptr(q),
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+                                          S, H, D, nb, bs, bt.shape[1], float(scale), _ptr(used))
+        if rc:
+            raise ValueError(f"oracle_decode_pairs failed ({rc})")
+        self.threads_used = int(used[0])
+        return out
+
+    # -- reshape_and_cache ----------------------------------------------------
+    def reshape_and_cache(self, key, value, k_cache, v_cache, slot_mapping):
+        """Writes into k_cache / v_cache in place (uint16 or float16 arrays)."""
+        key, value = _u16(key), _u16(value)
+        kc = k_cache.view(np.uint16) if k_cache.dtype == np.float16 else k_cache
+        vc = v_cache.view(np.uint16) if v_cache.dtype == np.float16 else v_cache
+        assert kc.flags.c_contiguous and vc.flags.c_contiguous
+        T, H, D = key.shape
+        nb, bs, nh, hd = kc.shape
+        assert (nh, hd) == (H, D)
+        sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        rc = self.lib.oracle_reshape_and_cache(_ptr(key), _ptr(value), _ptr(kc), _ptr(vc),
+                                               _ptr(sm), T, H, D, nb, bs)
+        if rc:
+            raise ValueError(f"oracle_reshape_and_cache failed ({rc})")
+
+
+_default = None
+
+
+def get():
+    """The oracle built from oracle/pa_oracle.c (built on first use if absent)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,298 @@
+/*
+ * Paged-attention decode oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * CPU definition that the GPU library is checked against.  Only the test
+ * suite, the smoke check and the CPU-baseline leg of the benchmark load it.
+ * It shares no code, header, table or helper with the GPU library, and the
+ * GPU library never loads it.
+ *
+ * Sources (web pages), cited by title and section:
+ *   [10x]  "vLLM推理加速深度解读：PagedAttention如何提升10x吞吐量"
+ *          §2.1  attention equation  Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V
+ *          §2.3  paged equations     Attention(Q,K_paged,V_paged) = softmax(Q K_paged^T / sqrt(d_k)) V_paged
+ *                                    K_paged[i] = K_physical[BlockTable[i / B]][i mod B]
+ *          §4.2  cache layout in the kernel sketch: K_cache, V_cache are
+ *                [num_blocks, block_size, num_heads, head_size]; Q and the
+ *                output are [num_heads, head_size] per sequence
+ *   [eng]  "深入解析LLM推理引擎：从PagedAttention到调度优化"
+ *          §3.2  block table worked example (block size 4, table [0, 1, 3, ...])
+ *          §3.3  the gather is driven by block_table and current_position
+ *
+ * Arithmetic: every fp16 value is decoded exactly to double (IEEE-754
+ * binary16 definition, written out below) and all arithmetic is in double.
+ * The softmax is the two-pass stable form: subtract the maximum logit,
+ * exponentiate, normalise.  Sums run in logical token order.
+ *
+ * Readings where the pages are silent:
+ *   - scale is an argument (the configurations pass 1/sqrt(head_dim));
+ *   - only logical positions 0 .. context_len-1 are attended;
+ *   - context_len == 0 gives an all-zero output;
+ *   - a slot (reshape_and_cache) is physical_block * block_size + offset;
+ *     slots outside [0, num_blocks*block_size) are not written.
+ *
+ * Parity pins for every function here live in the CPU test suite; there is
+ * no "parity unpinned" function in this file.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_OK 0
+#define OR_ERR_ARG (-1)
+#define OR_ERR_RANGE (-2)
+#define OR_ERR_NOMEM (-3)
+
+/* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * exponent 0: subnormal, value = fraction * 2^-24; exponent 31: Inf / NaN;
+ * otherwise value = (1024 + fraction) * 2^(exponent - 25). */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+/* Decode n binary16 values (used by the exhaustive decoder pin). */
+void oracle_half_array_to_double(const uint16_t *src, double *dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = oracle_half_to_double(src[i]);
+}
+
+/* Element (block, offset, head, d) of a [num_blocks, block_size, num_heads,
+ * head_dim] cache ([10x] §4.2). */
+static size_t cache_index(int64_t block, int64_t offset, int64_t head, int64_t d,
+                          int64_t block_size, int64_t num_heads, int64_t head_dim)
+{
+    return (size_t)(((block * block_size + offset) * num_heads + head) * head_dim + d);
+}
+
+/*
+ * The paged gather of [10x] §2.3: for logical position i of sequence s,
+ * K_paged[i] = K_physical[BlockTable[i / B]][i mod B], and the same for V.
+ * Writes the contiguous K_paged, V_paged rows of head h, shape
+ * [context_len, head_dim], as doubles.  Returns the number of rows, or a
+ * negative code when a table entry or the context length is out of range.
+ */
+int oracle_gather(double *k_out, double *v_out,
+                  const uint16_t *k_cache, const uint16_t *v_cache,
+                  const int32_t *block_tables, const int32_t *context_lens,
+                  int32_t seq, int32_t head,
+                  int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                  int32_t block_size, int32_t max_blocks_per_seq)
+{
+    int32_t L = context_lens[seq];
+    if (L < 0 || (int64_t)L > (int64_t)max_blocks_per_seq * block_size)
+        return OR_ERR_RANGE;
+    for (int32_t i = 0; i < L; ++i) {
+        int32_t logical_block = i / block_size;
+        int32_t offset = i % block_size;
+        int32_t physical = block_tables[(int64_t)seq * max_blocks_per_seq + logical_block];
+        if (physical < 0 || physical >= num_blocks)
+            return OR_ERR_RANGE;
+        for (int32_t d = 0; d < head_dim; ++d) {
+            size_t src = cache_index(physical, offset, head, d, block_size, num_heads, head_dim);
+            k_out[(int64_t)i * head_dim + d] = oracle_half_to_double(k_cache[src]);
+            v_out[(int64_t)i * head_dim + d] = oracle_half_to_double(v_cache[src]);
+        }
+    }
+    return L;
+}
+
+/*
+ * softmax(q K^T * scale) V for one query row against L contiguous key/value
+ * rows ([10x] §2.1 with 1/sqrt(d_k) passed in as scale).  Two-pass stable
+ * softmax; out has head_dim entries.  L == 0 gives zeros.
+ */
+static void attend_contiguous(double *out, const double *q, const double *K, const double *V,
+                              int32_t L, int32_t head_dim, double scale, double *logits)
+{
+    for (int32_t d = 0; d < head_dim; ++d)
+        out[d] = 0.0;
+    if (L == 0)
+        return;
+    for (int32_t i = 0; i < L; ++i) {
+        double dot = 0.0;
+        for (int32_t d = 0; d < head_dim; ++d)
+            dot += q[d] * K[(int64_t)i * head_dim + d];
+        logits[i] = dot * scale;
+    }
+    double m = logits[0];
+    for (int32_t i = 1; i < L; ++i)
+        if (logits[i] > m)
+            m = logits[i];
+    double Z = 0.0;
+    for (int32_t i = 0; i < L; ++i) {
+        logits[i] = exp(logits[i] - m);
+        Z += logits[i];
+    }
+    for (int32_t i = 0; i < L; ++i) {
+        double w = logits[i] / Z;
+        for (int32_t d = 0; d < head_dim; ++d)
+            out[d] += w * V[(int64_t)i * head_dim + d];
+    }
+}
+
+/* One (sequence, head): gather, then attend.  Scratch buffers are owned by
+ * the caller (one set per thread). */
+static int decode_one(double *out, const uint16_t *q,
+                      const uint16_t *k_cache, const uint16_t *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      int32_t s, int32_t h,
+                      int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                      int32_t block_size, int32_t max_blocks_per_seq, double scale,
+                      double *Kbuf, double *Vbuf, double *qbuf, double *logits)
+{
+    int L = oracle_gather(Kbuf, Vbuf, k_cache, v_cache, block_tables, context_lens, s, h,
+                          num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq);
+    if (L < 0)
+        return L;
+    const uint16_t *qrow = q + ((int64_t)s * num_heads + h) * head_dim;
+    for (int32_t d = 0; d < head_dim; ++d)
+        qbuf[d] = oracle_half_to_double(qrow[d]);
+    attend_contiguous(out, qbuf, Kbuf, Vbuf, L, head_dim, scale, logits);
+    return OR_OK;
+}
+
+static int check_shapes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                        int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq)
+{
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0)
+        return OR_ERR_ARG;
+    return OR_OK;
+}
+
+/*
+ * Decode a list of (sequence, head) pairs.  pairs holds 2*num_pairs int32
+ * values (s0, h0, s1, h1, ...); out is [num_pairs, head_dim] doubles.
+ * q is [num_seqs, num_heads, head_dim] binary16, block_tables is
+ * [num_seqs, max_blocks_per_seq] int32, context_lens is [num_seqs] int32.
+ * Pairs are independent; OpenMP spreads them over the host threads.
+ * *threads_used (if not NULL) receives the thread count.
+ */
+int oracle_decode_pairs(double *out, const int32_t *pairs, int32_t num_pairs,
+                        const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                        const int32_t *block_tables, const int32_t *context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                        int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                        double scale, int32_t *threads_used)
+{
+    int rc = check_shapes(num_seqs, num_heads, head_dim, num_blocks, block_size,
+                          max_blocks_per_seq);
+    if (rc)
+        return rc;
+    int64_t max_len = (int64_t)max_blocks_per_seq * block_size;
+    int status = OR_OK;
+    int nthreads = 1;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        nthreads = omp_get_num_threads();
+#endif
+        double *Kbuf = malloc(sizeof(double) * (size_t)(max_len * head_dim + 1));
+        double *Vbuf = malloc(sizeof(double) * (size_t)(max_len * head_dim + 1));
+        double *qbuf = malloc(sizeof(double) * (size_t)head_dim);
+        double *logits = malloc(sizeof(double) * (size_t)(max_len + 1));
+        int local = (Kbuf && Vbuf && qbuf && logits) ? OR_OK : OR_ERR_NOMEM;
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t p = 0; p < num_pairs; ++p) {
+            if (local)
+                continue;
+            int32_t s = pairs[2 * p], h = pairs[2 * p + 1];
+            if (s < 0 || s >= num_seqs || h < 0 || h >= num_heads) {
+                local = OR_ERR_ARG;
+                continue;
+            }
+            int r = decode_one(out + (int64_t)p * head_dim, q, k_cache, v_cache, block_tables,
+                               context_lens, s, h, num_heads, head_dim, num_blocks, block_size,
+                               max_blocks_per_seq, scale, Kbuf, Vbuf, qbuf, logits);
+            if (r)
+                local = r;
+        }
+        if (local) {
+#pragma omp critical
+            status = local;
+        }
+        free(Kbuf);
+        free(Vbuf);
+        free(qbuf);
+        free(logits);
+    }
+    if (threads_used)
+        *threads_used = nthreads;
+    return status;
+}
+
+/* Decode every (sequence, head): out is [num_seqs, num_heads, head_dim]. */
+int oracle_decode(double *out, const uint16_t *q, const uint16_t *k_cache,
+                  const uint16_t *v_cache, const int32_t *block_tables,
+                  const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                  int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                  int32_t max_blocks_per_seq, double scale, int32_t *threads_used)
+{
+    int rc = check_shapes(num_seqs, num_heads, head_dim, num_blocks, block_size,
+                          max_blocks_per_seq);
+    if (rc)
+        return rc;
+    int64_t n = (int64_t)num_seqs * num_heads;
+    int32_t *pairs = malloc(sizeof(int32_t) * (size_t)(2 * n + 2));
+    if (!pairs)
+        return OR_ERR_NOMEM;
+    for (int64_t i = 0; i < n; ++i) {
+        pairs[2 * i] = (int32_t)(i / num_heads);
+        pairs[2 * i + 1] = (int32_t)(i % num_heads);
+    }
+    rc = oracle_decode_pairs(out, pairs, (int32_t)n, q, k_cache, v_cache, block_tables,
+                             context_lens, num_seqs, num_heads, head_dim, num_blocks, block_size,
+                             max_blocks_per_seq, scale, threads_used);
+    free(pairs);
+    return rc;
+}
+
+/*
+ * Write each new token's key/value into its cache slot, as raw 16-bit
+ * patterns.  key, value: [num_tokens, num_heads, head_dim]; slot_mapping:
+ * [num_tokens] int64, slot = physical_block * block_size + offset, the
+ * position [10x] §2.3 maps a logical index to.  Slots outside
+ * [0, num_blocks * block_size) are skipped.
+ */
+int oracle_reshape_and_cache(const uint16_t *key, const uint16_t *value,
+                             uint16_t *k_cache, uint16_t *v_cache,
+                             const int64_t *slot_mapping, int32_t num_tokens,
+                             int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                             int32_t block_size)
+{
+    if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
+        return OR_ERR_ARG;
+    int64_t num_slots = (int64_t)num_blocks * block_size;
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= num_slots)
+            continue;
+        int64_t block = slot / block_size;
+        int64_t offset = slot % block_size;
+        for (int32_t h = 0; h < num_heads; ++h)
+            for (int32_t d = 0; d < head_dim; ++d) {
+                size_t dst = cache_index(block, offset, h, d, block_size, num_heads, head_dim);
+                size_t src = (size_t)(((int64_t)t * num_heads + h) * head_dim + d);
+                k_cache[dst] = key[src];
+                v_cache[dst] = value[src];
+            }
+    }
+    return OR_OK;
+}

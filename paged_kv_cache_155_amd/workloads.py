@@ -1,0 +1,278 @@
+"""Seeded synthetic inputs for paged-attention decode.
+
+This module only draws inputs: random lengths, block tables, fp16 tensors and
+the slots a block manager would hand out.  It holds none of the attention
+arithmetic and imports neither the GPU binding nor the CPU oracle, so both
+sides are fed the very same host bytes.
+
+Shapes follow the pages' models: LLaMA-7B (32 heads of 128, "深入解析LLM推理引擎"
+§2.1) and LLaMA-13B (40 heads of 128, "vLLM推理加速深度解读" §2.1); block
+sizes 16 and 32 ("vLLM推理加速深度解读" §2.3).  Physical block ids come from a
+seeded permutation without replacement, which is what popping a free list in
+random order produces ("深入解析LLM推理引擎" §3.3).
+
+Random streams: numpy PCG64.  Lengths, queries and new tokens come from
+children of SeedSequence([155, config, variant]); the block table, K/V pools,
+outlier picks and free-slot picks from children of SeedSequence([155, config,
+variant, block size]).  Every array has its own child stream.  Normals are drawn in
+float32 and rounded to fp16 (round to nearest even).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+SEED = 155
+_CHUNK = 1 << 22  # elements per drawing chunk (bounds the float32 temporary)
+
+DESCRIPTIONS = {
+    0: "tiny: 4 seqs ctx {1,17,33,100}, 4 heads x 64, B=16, pool 64 blocks",
+    1: "LLaMA-7B layer: 64 seqs ctx U[1,2048], 32 heads x 128, B=16",
+    2: "LLaMA-13B layer: 256 seqs ctx 70% U[16,512] / 30% U[512,4096], 40 heads x 128",
+    3: "shared prefix: 128 seqs, 32-block (512-token) common prefix + U[1,512] suffix, "
+       "32 heads x 128, B=16",
+    4: "long context: 8 seqs ctx 32768, 32 heads x 128, B=16, 1% x8 key outliers, P=512",
+}
+
+
+@dataclasses.dataclass
+class Workload:
+    """One decode step of one layer, as host arrays (fp16 stored as np.float16)."""
+    name: str
+    config: int
+    num_seqs: int
+    num_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    partition_size: int
+    scale: np.float32
+    q: np.ndarray             # [S, H, D] fp16
+    k_cache: np.ndarray       # [NB, B, H, D] fp16 (before the new tokens are written)
+    v_cache: np.ndarray       # [NB, B, H, D] fp16
+    block_tables: np.ndarray  # [S, MB] int32 (entries past the context: poison block)
+    context_lens: np.ndarray  # [S] int32 (counts the token written this step)
+    key: np.ndarray           # [T, H, D] fp16 new keys
+    value: np.ndarray         # [T, H, D] fp16 new values
+    slot_mapping: np.ndarray  # [T] int64
+    poison_block: int         # block id filled with NaN, used to pad the tables
+    ref_counts: np.ndarray    # [NB] int32 table references per physical block
+
+    @property
+    def num_tokens(self):
+        return int(self.slot_mapping.shape[0])
+
+    def kv_bytes(self):
+        """K+V bytes the decode must read: sum of context lengths x H x D x 2 x 2."""
+        return kv_bytes_per_token(self.num_heads, self.head_dim) * int(self.context_lens.sum())
+
+    def unique_kv_bytes(self):
+        """K+V bytes of the distinct (physical block, position) slots read."""
+        B = self.block_size
+        used = {}  # physical block -> most positions any sequence reads from it
+        for s in range(self.num_seqs):
+            L = int(self.context_lens[s])
+            for j in range((L + B - 1) // B):
+                pb = int(self.block_tables[s, j])
+                used[pb] = max(used.get(pb, 0), min(B, L - j * B))
+        return kv_bytes_per_token(self.num_heads, self.head_dim) * sum(used.values())
+
+
+def kv_bytes_per_token(num_heads, head_dim, dtype_bytes=2):
+    """Bytes of K plus V for one token in one layer: 2 x heads x head_dim x dtype."""
+    return 2 * num_heads * head_dim * dtype_bytes
+
+
+def _threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _normal_f16(seq, shape):
+    """N(0,1) fp16 array; chunk c of _CHUNK elements is drawn from the child
+    stream SeedSequence(seq.entropy, spawn_key=seq.spawn_key + (c,)), so the
+    values do not depend on the thread count."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float16)
+
+    def fill(c):
+        g = np.random.Generator(np.random.PCG64(
+            np.random.SeedSequence(seq.entropy, spawn_key=tuple(seq.spawn_key) + (c,))))
+        i = c * _CHUNK
+        out[i:i + min(_CHUNK, n - i)] = g.standard_normal(min(_CHUNK, n - i), dtype=np.float32)
+
+    chunks = range(-(-n // _CHUNK))
+    if n > _CHUNK:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, chunks))
+    else:
+        for c in chunks:
+            fill(c)
+    return out.reshape(shape)
+
+
+_SEQ_STREAMS = ["lens", "q", "newk", "newv"]
+_POOL_STREAMS = ["table", "k", "v", "outlier", "slots"]
+
+
+def _streams(config, block_size, variant):
+    """Per-sequence draws depend on (config, variant) only, so both block
+    sizes of a configuration see the same lengths and queries; pool draws
+    also depend on the block size."""
+    seq = np.random.SeedSequence([SEED, config, variant])
+    pool = np.random.SeedSequence([SEED, config, variant, block_size])
+    st = dict(zip(_SEQ_STREAMS, seq.spawn(len(_SEQ_STREAMS))))
+    st.update(zip(_POOL_STREAMS, pool.spawn(len(_POOL_STREAMS))))
+    return st
+
+
+def _gen(seq):
+    return np.random.Generator(np.random.PCG64(seq))
+
+
+def _draw_lengths(config, S, rng):
+    if config == 0:
+        return np.array([1, 17, 33, 100], dtype=np.int64)[:S]
+    if config == 1:
+        return rng.integers(1, 2048, size=S, endpoint=True)
+    if config == 2:
+        short = rng.integers(16, 512, size=S, endpoint=True)
+        long_ = rng.integers(512, 4096, size=S, endpoint=True)
+        pick_short = rng.random(S) < 0.7
+        return np.where(pick_short, short, long_)
+    if config == 3:
+        return 512 + rng.integers(1, 512, size=S, endpoint=True)
+    if config == 4:
+        return np.full(S, 32768, dtype=np.int64)
+    raise ValueError(config)
+
+
+_SHAPES = {  # config -> (S, H, D, B default, max context, partition size)
+    0: (4, 4, 64, 16, 100, 512),
+    1: (64, 32, 128, 16, 2048, 512),
+    2: (256, 40, 128, 16, 4096, 512),
+    3: (128, 32, 128, 16, 1024, 512),
+    4: (8, 32, 128, 16, 32768, 512),
+}
+
+
+def make_workload(config, block_size=None, num_seqs=None, num_heads=None, variant=0,
+                  poison=True, partition_size=None):
+    """Draw one configuration.
+
+    num_seqs / num_heads shrink a configuration for quick parity runs while
+    keeping its length distribution, block size and table structure.
+    poison=True fills every slot that must never be read (positions at or
+    past a sequence's context in its last block, the table padding block and
+    the slot about to receive the new token) with fp16 NaN.
+    """
+    S0, H0, D, B0, max_ctx, P0 = _SHAPES[config]
+    S = S0 if num_seqs is None else int(num_seqs)
+    H = H0 if num_heads is None else int(num_heads)
+    B = B0 if block_size is None else int(block_size)
+    P = P0 if partition_size is None else int(partition_size)
+    st = _streams(config, B, variant)
+    MB = -(-max_ctx // B)
+
+    lens = _draw_lengths(config, S, _gen(st["lens"])).astype(np.int64)
+    if config == 3:
+        n_prefix = 512 // B
+        suffix_blocks = [-(-(int(L) - 512) // B) for L in lens]
+        needed = n_prefix + sum(suffix_blocks)
+    else:
+        n_prefix = 0
+        needed = sum(-(-int(L) // B) for L in lens)
+    NB = 64 if config == 0 else int(math.ceil(1.1 * needed))
+    NB = max(NB, needed + 1)  # at least one spare block for the poison padding
+    perm = _gen(st["table"]).permutation(NB).astype(np.int64)
+
+    tables = np.empty((S, MB), dtype=np.int32)
+    cursor = 0
+    prefix_ids = perm[:n_prefix]
+    cursor = n_prefix
+    owned = []
+    for s in range(S):
+        L = int(lens[s])
+        if config == 3:
+            nsuf = -(-(L - 512) // B)
+            ids = np.concatenate([prefix_ids, perm[cursor:cursor + nsuf]])
+            cursor += nsuf
+        else:
+            n = -(-L // B)
+            ids = perm[cursor:cursor + n]
+            cursor += n
+        owned.append(ids)
+    poison_block = int(perm[cursor])
+    cursor += 1
+    for s in range(S):
+        tables[s, :] = poison_block
+        tables[s, :len(owned[s])] = owned[s]
+
+    ref = np.zeros(NB, dtype=np.int32)
+    for s in range(S):
+        np.add.at(ref, owned[s].astype(np.int64), 1)
+    if config == 3:
+        assert np.all(ref[prefix_ids] == S), "shared prefix blocks must be referenced by all"
+
+    q = _normal_f16(st["q"], (S, H, D))
+    k_cache = _normal_f16(st["k"], (NB, B, H, D))
+    v_cache = _normal_f16(st["v"], (NB, B, H, D))
+    T = S
+    key = _normal_f16(st["newk"], (T, H, D))
+    value = _normal_f16(st["newv"], (T, H, D))
+
+    if config == 4:
+        # 1% of (physical slot, head) key vectors scaled by 8 (exact in fp16)
+        rng = _gen(st["outlier"])
+        for arr in (k_cache, key):
+            flat = arr.reshape(-1, D)
+            sel = rng.random(flat.shape[0]) < 0.01
+            flat[sel] = flat[sel] * np.float16(8)
+
+    if config == 0:
+        # the new tokens go to random free slots: slots that hold none of the
+        # live positions and are not in the poison block
+        live = np.zeros(NB * B, dtype=bool)
+        for s in range(S):
+            for i in range(int(lens[s])):
+                live[int(tables[s, i // B]) * B + i % B] = True
+        live[poison_block * B:(poison_block + 1) * B] = True
+        free = np.flatnonzero(~live)
+        T = 4
+        key, value = key[:T], value[:T]
+        slots = _gen(st["slots"]).choice(free, size=T, replace=False).astype(np.int64)
+    else:
+        # one new token per sequence at logical position ctx-1: the slot the
+        # block manager assigned to that position
+        pos = lens - 1
+        slots = np.array([int(tables[s, pos[s] // B]) * B + int(pos[s] % B) for s in range(S)],
+                         dtype=np.int64)
+
+    if poison:
+        nan = np.float16(np.nan)
+        k_cache[poison_block] = nan
+        v_cache[poison_block] = nan
+        for s in range(S):
+            L = int(lens[s])
+            if L % B:
+                last = int(tables[s, (L - 1) // B])
+                if config != 3 or (L - 1) // B >= n_prefix:
+                    k_cache[last, L % B:] = nan
+                    v_cache[last, L % B:] = nan
+        if config != 0:
+            kf = k_cache.reshape(NB * B, H, D)
+            vf = v_cache.reshape(NB * B, H, D)
+            kf[slots] = nan
+            vf[slots] = nan
+
+    return Workload(
+        name=f"config{config}" + (f"_B{B}" if block_size else ""),
+        config=config, num_seqs=S, num_heads=H, head_dim=D, block_size=B, num_blocks=NB,
+        max_blocks_per_seq=MB, partition_size=P, scale=np.float32(1.0 / math.sqrt(D)),
+        q=q, k_cache=k_cache, v_cache=v_cache, block_tables=tables,
+        context_lens=lens.astype(np.int32), key=key, value=value, slot_mapping=slots,
+        poison_block=poison_block, ref_counts=ref)

@@ -1,0 +1,73 @@
+"""Plausible mistakes planted in a copy of the oracle must each fail a pin.
+
+Every mutant below is a one-spot textual change to oracle/pa_oracle.c,
+compiled into a temporary library and checked by running oracle_pins.py
+against it in a child process (a mutant may read out of bounds, so it never
+runs inside the test process).  A mutant that passes every pin would mean
+the pins cannot see that mistake.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "pa_oracle.c")
+
+MUTANTS = {
+    "block_index_mod": ("int32_t logical_block = i / block_size;",
+                        "int32_t logical_block = i % block_size;"),
+    "offset_div": ("int32_t offset = i % block_size;", "int32_t offset = i / block_size;"),
+    "drop_last_token": ("for (int32_t i = 0; i < L; ++i) {\n        int32_t logical_block",
+                        "for (int32_t i = 0; i < L - 1; ++i) {\n        int32_t logical_block"),
+    "drop_first_token": ("for (int32_t i = 0; i < L; ++i) {\n        double w",
+                         "for (int32_t i = 1; i < L; ++i) {\n        double w"),
+    "no_scale": ("logits[i] = dot * scale;", "logits[i] = dot;"),
+    "exp_sign": ("logits[i] = exp(logits[i] - m);", "logits[i] = exp(m - logits[i]);"),
+    "no_max_shift": ("logits[i] = exp(logits[i] - m);", "logits[i] = exp(logits[i]);"),
+    "no_normalise": ("double w = logits[i] / Z;", "double w = logits[i];"),
+    "layout_head_offset_swapped": ("return (size_t)(((block * block_size + offset) * num_heads + head) * head_dim + d);",
+                                   "return (size_t)(((block * num_heads + head) * block_size + offset) * head_dim + d);"),
+    "value_from_key_cache": ("v_out[(int64_t)i * head_dim + d] = oracle_half_to_double(v_cache[src]);",
+                             "v_out[(int64_t)i * head_dim + d] = oracle_half_to_double(k_cache[src]);"),
+    "q_row_of_head0": ("const uint16_t *qrow = q + ((int64_t)s * num_heads + h) * head_dim;",
+                       "const uint16_t *qrow = q + ((int64_t)s * num_heads) * head_dim;"),
+    "dot_skips_last_dim": ("for (int32_t d = 0; d < head_dim; ++d)\n            dot += q[d]",
+                           "for (int32_t d = 0; d < head_dim - 1; ++d)\n            dot += q[d]"),
+    "half_bias": ("v = ldexp((double)(1024 + frac), expo - 25);",
+                  "v = ldexp((double)(1024 + frac), expo - 24);"),
+    "half_subnormal": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    "half_no_implicit_bit": ("v = ldexp((double)(1024 + frac), expo - 25);",
+                             "v = ldexp((double)frac, expo - 25);"),
+    "half_nan_as_inf": ("v = frac ? NAN : INFINITY;", "v = INFINITY;"),
+    "reshape_block_mod": ("int64_t block = slot / block_size;", "int64_t block = slot % block_size;"),
+    "reshape_no_upper_check": ("if (slot < 0 || slot >= num_slots)", "if (slot < 0)"),
+    "reshape_value_gets_key": ("v_cache[dst] = value[src];", "v_cache[dst] = key[src];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    sys.path.insert(0, ROOT)
+    from oracle import build as obuild
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not found exactly once"
+    src = tmp_path / f"{name}.c"
+    src.write_text(text.replace(old, new))
+    lib = obuild.build(str(src), str(tmp_path / f"lib{name}.so"), quiet=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), "--lib", lib],
+                       capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "OMP_NUM_THREADS": "2"})
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the same harness accepts the oracle as committed."""
+    sys.path.insert(0, ROOT)
+    from oracle import build as obuild
+    lib = obuild.build(SRC, str(tmp_path / "libcontrol.so"), quiet=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), "--lib", lib],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:]
