@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of one paged-attention decode step on one MI355X.
+
+A step is the whole hot path for one layer: pa_reshape_and_cache writes the
+step's new token of every sequence into its slot, then pa_decode (partition
+kernel + log-sum-exp reduce) attends over the paged K/V.  Inputs are seeded
+synthetic tensors, already resident in HBM when the timed region starts.
+
+    python bench.py [--steps K] [--warmup W] [--config 1] [--block-size B]
+                    [--partition-size P] [--no-cpu-baseline]
+
+Prints ONE JSON line.  value = K/V bytes the decode must read per step
+(sum of context lengths x heads x head_dim x 2 tensors x 2 bytes) divided
+by the measured step time, in GB/s; tokens/s/layer = sequences / step time.
+roofline: the decode (its HIP-event duration on the stream it runs on)
+against the 8 TB/s HBM3E peak.  cpu_baseline: the CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+
+`--probe copy` instead runs a plain copy of known size (reshape_and_cache
+over 1 GiB) for calibrating hardware byte counters.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged-attn decode KV-read GB/s (fraction of HBM peak); decode tokens/s/layer"
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=float, default=2.0e6,
+                    help="token-heads of oracle work in the CPU baseline sample")
+    ap.add_argument("--probe", choices=["copy"], default=None)
+    ap.add_argument("--probe-mib", type=int, default=1024)
+    return ap.parse_args()
+
+
+def _sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(config_name):
+    """Per-launch HBM bytes from committed counter runs, if they were taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(config_name)
+    except (ValueError, AttributeError):
+        return None
+    src = os.path.join(ROOT, "paged_kv_cache_155_amd", "csrc", "pa_decode.hip")
+    if not rec or rec.get("kernel_source_sha") != _sha(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def probe_copy(mib):
+    import torch
+    import paged_kv_cache_155_amd as pa
+    H, D = 32, 128
+    row = H * D * 2
+    T = mib * 1024 * 1024 // (2 * row)  # K and V together = mib MiB read
+    key = torch.randn(T, H, D, device="cuda").half()
+    val = torch.randn(T, H, D, device="cuda").half()
+    kc = torch.empty(T // 16, 16, H, D, dtype=torch.float16, device="cuda")
+    vc = torch.empty_like(kc)
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    for _ in range(3):
+        pa.reshape_and_cache(key, val, kc, vc, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(kc.view(-1), key.view(-1))
+    print(json.dumps({"probe": "copy", "kernel": "reshape_and_cache_kernel", "launches": 3,
+                      "read_bytes_per_launch": 2 * T * row + 8 * T,
+                      "write_bytes_per_launch": 2 * T * row}), flush=True)
+
+
+def cpu_baseline(w, sample_tokens):
+    """Time the oracle (as it stands) on a bounded, deterministic sample of
+    (sequence, head) pairs of the same workload; GB/s over the sampled
+    K/V bytes."""
+    import numpy as np
+    import oracle
+    from paged_kv_cache_155_amd.workloads import kv_bytes_per_token
+    orc = oracle.get()
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    orc.reshape_and_cache(w.key, w.value, kc, vc, w.slot_mapping)
+    S, H = w.num_seqs, w.num_heads
+    pairs = [(s, h) for s in range(S) for h in range(H)]
+    rng = np.random.default_rng(155)
+    order = rng.permutation(len(pairs))
+    chosen, tok = [], 0
+    for i in order:
+        if tok >= sample_tokens:
+            break
+        s, h = pairs[i]
+        chosen.append((s, h))
+        tok += int(w.context_lens[s])
+    t0 = time.perf_counter()
+    orc.decode_pairs(chosen, w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale))
+    dt = time.perf_counter() - t0
+    nbytes = tok * kv_bytes_per_token(1, w.head_dim)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": orc.threads_used,
+            "kind": "oracle",
+            "sample": f"{len(chosen)} of {len(pairs)} (sequence, head) pairs drawn with a seeded "
+                      f"permutation, {tok} token-heads, one fp64 oracle decode; "
+                      f"{dt:.2f} s wall, tokens/s/layer-equivalent "
+                      f"{len(chosen) / H / dt:.1f}"}
+
+
+def main():
+    a = _args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}): "
+              "this library is a single-GPU kernel; sharding is described, not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import DESCRIPTIONS, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pa.load()
+    if a.probe == "copy":
+        probe_copy(a.probe_mib)
+        return
+
+    w = make_workload(a.config, block_size=a.block_size, partition_size=a.partition_size,
+                      poison=False)
+    P = w.partition_size
+    dev = "cuda"
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    q, kc, vc = up(w.q), up(w.k_cache), up(w.v_cache)
+    bt, cl = up(w.block_tables), up(w.context_lens)
+    key, val, slots = up(w.key), up(w.value), up(w.slot_mapping)
+    out = torch.empty_like(q)
+    need = pa.decode_workspace_size(w.num_seqs, w.num_heads, w.head_dim, w.block_size,
+                                    w.max_blocks_per_seq, P)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    scale = float(w.scale)
+
+    def step():
+        pa.reshape_and_cache(key, val, kc, vc, slots)
+        pa.decode(out, q, kc, vc, bt, cl, scale, partition_size=P, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = a.steps
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        pa.reshape_and_cache(key, val, kc, vc, slots)
+        ev[i][1].record(stream)
+        pa.decode(out, q, kc, vc, bt, cl, scale, partition_size=P, workspace=ws)
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_begin.elapsed_time(t_end)
+    rc_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ms_step = total_ms / K
+    t_dec = float(np.mean(dec_ms))
+    t_rc = float(np.mean(rc_ms))
+    kvb = w.kv_bytes()
+    achieved = kvb / (t_dec * 1e-3) / 1e9
+    value = kvb / (ms_step * 1e-3) / 1e9
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": a.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {
+            "workload": f"config{a.config}: {DESCRIPTIONS[a.config]}",
+            "num_seqs": w.num_seqs, "num_heads": w.num_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "partition_size": P, "num_blocks": w.num_blocks,
+            "kv_bytes_per_step": kvb, "unique_kv_bytes": w.unique_kv_bytes(),
+            "decode_tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
+            "decode_only_tokens_per_s_per_layer": round(w.num_seqs / (t_dec * 1e-3), 1),
+            "t_decode_us_mean": round(t_dec * 1e3, 2),
+            "t_decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
+            "t_reshape_us_mean": round(t_rc * 1e3, 2),
+            "wall_s_timed": round(wall, 4), "accumulate": "f32",
+        },
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic(f"config{a.config}_B{w.block_size}_P{P}"),
+                     "kernel": "pa_decode (partition kernel + reduce kernel), HIP events"},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

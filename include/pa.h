@@ -1,0 +1,139 @@
+/*
+ * pa.h — C ABI of the paged-attention decode library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources (web pages), cited by title and section:
+ *   [10x]  "vLLM推理加速深度解读：PagedAttention如何提升10x吞吐量"
+ *          §2.1 attention equation; §2.3 paged attention equations and the
+ *          gather K_paged[i] = K_physical[BlockTable[i / B]][i mod B];
+ *          §4.2 cache layout [num_blocks, block_size, num_heads, head_size]
+ *   [eng]  "深入解析LLM推理引擎：从PagedAttention到调度优化"
+ *          §3.2 on-demand block filling and the block table; §3.3 the gather
+ *          driven by block_table and the current position
+ *   [arch] "vLLM基础架构：核心组件、PagedAttention原理、KV Cache管理与连续批处理机制"
+ *          §2.3 a new block every block_size tokens; shared prefix blocks
+ *
+ * Conventions shared by every entry point
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or synchronises; it keeps no state
+ *     between calls.  Work is enqueued on `stream` (a hipStream_t passed as
+ *     void*, NULL = the null stream) and runs asynchronously in stream order.
+ *   - fp16 means IEEE-754 binary16.  All arrays are dense, row-major, and
+ *     their base pointers are 16-byte aligned.
+ *   - K/V cache layout [num_blocks, block_size, num_heads, head_dim] ([10x]
+ *     §4.2), K and V in separate arrays.  A slot is
+ *     physical_block * block_size + offset_in_block.
+ *   - Return value: PA_OK (0) or a negative PA_ERR_* code.  Arguments are
+ *     checked on the host before anything is enqueued; a failed check
+ *     enqueues nothing.  Values that live on the device (block ids, context
+ *     lengths, slots) are preconditions and are not checked, since checking
+ *     them would need a synchronisation.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL                          */
+    PA_ERR_INVALID_DIM = -2, /* a size is <= 0 (num_tokens/num_seqs < 0) or overflows */
+    PA_ERR_UNSUPPORTED = -3, /* head_dim or block_size not compiled in               */
+    PA_ERR_PARTITION = -4,   /* partition_size not 0 and not a positive multiple of block_size */
+    PA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than pa_decode_workspace_size */
+    PA_ERR_ALIGN = -6,       /* a base pointer is not 16-byte aligned                */
+    PA_ERR_HIP = -7          /* the HIP runtime reported an error at launch          */
+};
+
+/*
+ * Write this step's new keys and values into their cache slots.
+ *
+ * The block manager gives the token at logical position p of a sequence the
+ * slot BlockTable[p / block_size] * block_size + p % block_size ([10x] §2.3
+ * gather equation read as a write; [eng] §3.2 and [arch] §2.3: a block fills
+ * position by position and a new block is taken every block_size tokens).
+ *
+ *   key, value    fp16 [num_tokens, num_heads, head_dim]        (read)
+ *   k_cache,
+ *   v_cache       fp16 [num_blocks, block_size, num_heads, head_dim] (written
+ *                 at the given slots only)
+ *   slot_mapping  int64 [num_tokens]: slot of each token.  A slot outside
+ *                 [0, num_blocks * block_size) — e.g. -1 for a padding
+ *                 token — is skipped.  Valid slots must be distinct within a
+ *                 call (otherwise which token lands there is unspecified).
+ *
+ * The copy is bit-exact: raw 16-bit patterns (NaN payloads, signed zeros,
+ * subnormals included) are moved, never converted.
+ * Requires head_dim % 8 == 0 (whole 16-byte vectors per head row).
+ * num_tokens == 0 enqueues nothing and returns PA_OK.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
+                         int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                         void* stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for the split-context path:
+ * fp32 partial results (output row, running maximum, running sum) for each
+ * (sequence, head, context partition).  Returns 0 when no split happens
+ * (partition_size == 0, or a single partition covers max_blocks_per_seq *
+ * block_size tokens) and 0 for invalid arguments.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t partition_size);
+
+/*
+ * Paged-attention decode, one query token per sequence ([10x] §2.3):
+ *   out[s,h,:] = softmax(scale * q[s,h,:] . K_paged[s,h,i,:]^T over
+ *                i < context_lens[s]) . V_paged[s,h,:,:]
+ * with K_paged[s,h,i] = k_cache[block_tables[s, i / block_size],
+ * i % block_size, h] and likewise V ([10x] §2.3; [eng] §3.3).  scale is
+ * the caller's 1/sqrt(d_k) ([10x] §2.1).  A physical block that several
+ * tables list (a shared prefix, [arch] §2.3) is simply read through each.
+ *
+ *   out           fp16 [num_seqs, num_heads, head_dim]              (written)
+ *   q             fp16 [num_seqs, num_heads, head_dim]              (read)
+ *   k_cache,
+ *   v_cache       fp16 [num_blocks, block_size, num_heads, head_dim] (read)
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; only the first
+ *                 ceil(context_lens[s] / block_size) entries of row s are
+ *                 read, and each must lie in [0, num_blocks).
+ *   context_lens  int32 [num_seqs]; 0 <= context_lens[s] <=
+ *                 max_blocks_per_seq * block_size.  0 gives an all-zero row.
+ *                 Cache positions at or past the context are never used in
+ *                 arithmetic, whatever they hold.
+ *   head_dim      64 or 128;  block_size  16 or 32.
+ *   partition_size  0: each (sequence, head) is one work unit.  Otherwise a
+ *                 positive multiple of block_size: the context is split into
+ *                 partitions of that many tokens, each reduced to (max, sum,
+ *                 normalised row), and a second kernel merges them with the
+ *                 log-sum-exp identity.
+ *   workspace, workspace_bytes  device scratch of at least
+ *                 pa_decode_workspace_size(...) bytes (may be NULL when that
+ *                 is 0).  Contents on entry do not matter.
+ *
+ * Arithmetic: fp16 inputs, fp32 products, sums and softmax; the result is
+ * rounded to fp16 (nearest even).  For fixed arguments the result is
+ * bitwise reproducible, and it does not depend on which physical blocks
+ * hold the data.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+              int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* pa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

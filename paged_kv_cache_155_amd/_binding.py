@@ -1,0 +1,140 @@
+"""ctypes binding of libpa.so (declared in include/pa.h).
+
+Argument marshalling only: shape/dtype/device checks, raw pointers and the
+current HIP stream.  torch supplies device memory and streams; every step of
+the computation runs in the library's HIP kernels.  There is no fallback:
+if libpa.so is missing or cannot be loaded, every call raises.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PA_LIB", os.path.join(_PKG, "libpa.so"))
+
+PA_OK = 0
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_lib = None
+
+
+class PAError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} ({code})")
+
+
+def load(path=None):
+    """Load (once) and return the ctypes handle on libpa.so."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(
+            f"HIP library not built: {p} is missing (build it with "
+            f"`python -m paged_kv_cache_155_amd._build` or __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    lib.pa_reshape_and_cache.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]
+    lib.pa_reshape_and_cache.restype = ctypes.c_int
+    lib.pa_decode_workspace_size.argtypes = [_I32] * 6
+    lib.pa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.pa_decode.argtypes = ([_P] * 6 + [_I32] * 6 + [ctypes.c_float, _I32, _P, ctypes.c_size_t,
+                                                       _P])
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(code):
+    return load().pa_status_string(int(code)).decode()
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype, shape=None, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
+    """Write key/value [T, H, D] fp16 into k_cache/v_cache [NB, B, H, D] at
+    slot_mapping [T] int64 (slot = block * B + offset; out-of-range slots,
+    e.g. -1, are skipped).  Bit-exact; enqueued on the current stream."""
+    import torch
+    _check(k_cache, "k_cache", torch.float16, ndim=4)
+    NB, B, H, D = k_cache.shape
+    _check(v_cache, "v_cache", torch.float16, shape=k_cache.shape)
+    _check(key, "key", torch.float16, ndim=3)
+    T = key.shape[0]
+    _check(key, "key", torch.float16, shape=(T, H, D))
+    _check(value, "value", torch.float16, shape=(T, H, D))
+    _check(slot_mapping, "slot_mapping", torch.int64, shape=(T,))
+    rc = load().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(slot_mapping), T, H, D, NB, B, _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_reshape_and_cache")
+
+
+def decode_workspace_size(num_seqs, num_heads, head_dim, block_size, max_blocks_per_seq,
+                          partition_size):
+    return int(load().pa_decode_workspace_size(num_seqs, num_heads, head_dim, block_size,
+                                               max_blocks_per_seq, partition_size))
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, partition_size=512,
+           workspace=None, stream=None):
+    """Paged-attention decode into out [S, H, D] fp16 (returned).
+
+    q [S, H, D] fp16; k_cache/v_cache [NB, B, H, D] fp16; block_tables
+    [S, MB] int32; context_lens [S] int32; partition_size 0 (no split) or a
+    multiple of B.  workspace: uint8 GPU tensor of at least
+    decode_workspace_size(...) bytes, allocated here if None."""
+    import torch
+    _check(k_cache, "k_cache", torch.float16, ndim=4)
+    NB, B, H, D = k_cache.shape
+    _check(v_cache, "v_cache", torch.float16, shape=k_cache.shape)
+    _check(q, "q", torch.float16, ndim=3)
+    S = q.shape[0]
+    _check(q, "q", torch.float16, shape=(S, H, D))
+    _check(out, "out", torch.float16, shape=(S, H, D))
+    _check(block_tables, "block_tables", torch.int32, ndim=2)
+    MB = block_tables.shape[1]
+    _check(block_tables, "block_tables", torch.int32, shape=(S, MB))
+    _check(context_lens, "context_lens", torch.int32, shape=(S,))
+    need = decode_workspace_size(S, H, D, B, MB, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if need else None
+    elif need:
+        _check(workspace, "workspace", torch.uint8, ndim=1)
+    wbytes = workspace.numel() if workspace is not None else 0
+    rc = load().pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                          _ptr(context_lens), S, H, D, NB, B, MB, float(scale), int(partition_size),
+                          _ptr(workspace), wbytes, _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_decode")
+    return out

@@ -1,0 +1,167 @@
+// C ABI of the paged-attention decode library: host-side argument checks,
+// workspace sizing and launches on the caller's stream.  The semantics of
+// every entry point are documented with its declaration in pa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Number of context partitions the grid covers, or -1 for bad arguments.
+int64_t num_partitions(int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size)
+{
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * block_size;
+    if (partition_size == 0)
+        return 1;
+    return (max_tokens + partition_size - 1) / partition_size;
+}
+
+bool supported_decode(int32_t head_dim, int32_t block_size)
+{
+    return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
+}
+
+struct WorkspaceLayout {
+    size_t o_bytes, m_bytes, l_bytes, total;
+};
+
+WorkspaceLayout layout(int64_t units, int32_t head_dim)
+{
+    auto round256 = [](size_t b) { return (b + 255) & ~size_t(255); };
+    WorkspaceLayout w;
+    w.o_bytes = round256((size_t)units * head_dim * sizeof(float));
+    w.m_bytes = round256((size_t)units * sizeof(float));
+    w.l_bytes = round256((size_t)units * sizeof(float));
+    w.total = w.o_bytes + w.m_bytes + w.l_bytes;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status)
+{
+    switch (status) {
+    case PA_OK: return "PA_OK: success";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_INVALID_DIM: return "PA_ERR_INVALID_DIM: a size is out of range";
+    case PA_ERR_UNSUPPORTED:
+        return "PA_ERR_UNSUPPORTED: head_dim must be 64 or 128 and block_size 16 or 32";
+    case PA_ERR_PARTITION:
+        return "PA_ERR_PARTITION: partition_size must be 0 or a positive multiple of block_size";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a base pointer is not 16-byte aligned";
+    case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown pa status";
+    }
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
+                         int32_t head_dim, int32_t num_blocks, int32_t block_size, void* stream)
+{
+    if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
+        return PA_ERR_INVALID_DIM;
+    if (head_dim % 8 != 0)
+        return PA_ERR_UNSUPPORTED;
+    if ((int64_t)num_heads * head_dim / 8 > INT32_MAX)
+        return PA_ERR_INVALID_DIM;
+    if (num_tokens == 0)
+        return PA_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+        return PA_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+        return PA_ERR_ALIGN;
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    const int32_t row_vectors = num_heads * head_dim / 8;
+    hipError_t e = pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
+                                                num_tokens, num_slots, row_vectors,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t partition_size)
+{
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks_per_seq <= 0 || partition_size < 0)
+        return 0;
+    if (partition_size % block_size != 0)
+        return 0;
+    const int64_t np = num_partitions(block_size, max_blocks_per_seq, partition_size);
+    if (np <= 1)
+        return 0;
+    return layout((int64_t)num_seqs * num_heads * np, head_dim).total;
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+              int32_t max_blocks_per_seq, float scale, int32_t partition_size, void* workspace,
+              size_t workspace_bytes, void* stream)
+{
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0 ||
+        max_blocks_per_seq <= 0)
+        return PA_ERR_INVALID_DIM;
+    if (!supported_decode(head_dim, block_size))
+        return PA_ERR_UNSUPPORTED;
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+        return PA_ERR_INVALID_DIM;
+    if (partition_size < 0 || partition_size % block_size != 0)
+        return PA_ERR_PARTITION;
+    if (!std::isfinite(scale))
+        return PA_ERR_INVALID_DIM;
+    if (num_seqs == 0)
+        return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+        return PA_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+        (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+        return PA_ERR_ALIGN;
+
+    const int64_t np = num_partitions(block_size, max_blocks_per_seq, partition_size);
+    const int64_t units = (int64_t)num_seqs * num_heads * np;
+    if (units > INT32_MAX || (int64_t)num_seqs * num_heads > INT32_MAX)
+        return PA_ERR_INVALID_DIM;
+
+    pa::DecodeParams p{};
+    p.out = static_cast<_Float16*>(out);
+    p.q = static_cast<const _Float16*>(q);
+    p.k_cache = static_cast<const _Float16*>(k_cache);
+    p.v_cache = static_cast<const _Float16*>(v_cache);
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.partition_size = np == 1 ? max_blocks_per_seq * block_size : partition_size;
+    p.num_partitions = (int32_t)np;
+    p.total_units = (uint32_t)units;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
+    if (np > 1) {
+        const WorkspaceLayout w = layout(units, head_dim);
+        if (!workspace || workspace_bytes < w.total)
+            return PA_ERR_WORKSPACE;
+        if (!aligned16(workspace))
+            return PA_ERR_ALIGN;
+        char* base = static_cast<char*>(workspace);
+        p.ws_o = reinterpret_cast<float*>(base);
+        p.ws_m = reinterpret_cast<float*>(base + w.o_bytes);
+        p.ws_l = reinterpret_cast<float*>(base + w.o_bytes + w.m_bytes);
+    }
+    hipError_t e = pa::launch_decode_dispatch(p, head_dim, block_size,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,398 @@
+// Paged-attention decode kernels for gfx950 (MI355X), fp16 KV, fp32 math.
+//
+// Sources (web pages), cited by title and section:
+//   [10x]  "vLLM推理加速深度解读：PagedAttention如何提升10x吞吐量"
+//          §2.1 attention equation; §2.3 paged attention and the gather
+//          K_paged[i] = K_physical[BlockTable[i / B]][i mod B];
+//          §4.2 kernel strategy (walk the context block by block, keep the
+//          block table close, one group of lanes per query head) and the
+//          cache layout [num_blocks, block_size, num_heads, head_size]
+//   [eng]  "深入解析LLM推理引擎：从PagedAttention到调度优化" §3.3 (the
+//          gather follows block_table up to the current position)
+//
+// Design on CDNA4 (decode with one query per head is a batched GEMV: every
+// K/V byte is used once, so the bound is HBM bandwidth and MFMA has nothing
+// to do):
+//   * one workgroup (4 waves) per (sequence, head, context partition); the
+//     hardware workgroup id is remapped so that each of the 8 XCDs, which
+//     receive workgroups round-robin, gets a contiguous range of heads
+//     (physical blocks shared between sequences then meet in one L2);
+//   * a wave walks 32-token tiles (64 for head_dim 64).  For head_dim 128 a
+//     token's row of one head is 256 contiguous bytes = 16 lanes x 16 bytes,
+//     so one global_load_dwordx4 covers 4 tokens; a tile issues 8 K loads
+//     and 8 V loads per lane before any arithmetic;
+//   * block ids: each wave reads up to 64 table entries with one vector load
+//     and pulls the one a load needs with v_readlane (a scalar), so the
+//     K/V address of a whole load is scalar base + lane offset;
+//   * q.k with v_dot2_f32_f16 (fp16 products, fp32 sum), then a 16-lane
+//     DPP butterfly (quad_perm, row_half_mirror, row_mirror) - no LDS;
+//   * online softmax per lane group (running max m, sum l, fp32 row
+//     accumulator, rescaled once per tile), merged across lane groups with
+//     shuffles and across waves through 2 KB of LDS, in fixed order;
+//   * base-2 exponent: logits are scaled by scale*log2(e) and exponentiated
+//     with v_exp_f32;
+//   * split context: each partition writes (m, l, normalised row) to the
+//     workspace; pa_reduce merges them with the log-sum-exp identity.
+//     A single-partition (sequence, head) writes its fp16 row directly.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kLoads = 8;  // K (and V) 16-byte loads per lane per tile
+constexpr float kNegInf = -__builtin_inff();
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of kLanes lanes (8 or 16); every lane of a group
+// ends with the group sum.  quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror.
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    if constexpr (kLanes == 16)
+        v += dpp_mov<0x140>(v);
+    return v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int readlane(int v, int lane)
+{
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Hardware workgroup i of n lands on XCD i % 8.  Give XCD x the contiguous
+// logical range [x*n/8, (x+1)*n/8) (remainder spread over the first XCDs).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n)
+{
+    constexpr uint32_t kXcds = 8;
+    const uint32_t q = n / kXcds, r = n % kXcds;
+    const uint32_t xcd = i % kXcds, k = i / kXcds;
+    return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
+struct LaneState {
+    float m;       // running maximum of base-2 logits (group-uniform)
+    float l;       // running sum of exp2(logit - m)
+    float acc[8];  // running sum of exp2(logit - m) * v over this lane's 8 columns
+};
+
+template <int D, int B>
+struct Geometry {
+    static constexpr int kLanesPerToken = D / 8;              // 16 B per lane
+    static constexpr int kTokensPerLoad = kWave / kLanesPerToken;
+    static constexpr int kTile = kLoads * kTokensPerLoad;     // tokens per wave step
+    static_assert(kTile % B == 0 || B % kTile == 0, "tile / block mismatch");
+    static_assert(B % kTokensPerLoad == 0, "a load must stay in one block");
+};
+
+struct TileCtx {
+    const _Float16* k;
+    const _Float16* v;
+    int64_t block_elems;  // B * H * D
+    int lane_elem;        // (g * H + h) * D + lt * 8, for in-block offset 0
+    int token_stride;     // H * D elements between consecutive in-block offsets
+    int group;            // lane / lanes-per-token
+    int end;              // first logical position not attended by this partition
+    float scale_log2;
+    h2 q[4];
+};
+
+// One tile of kTile tokens starting at logical position t0 (a multiple of
+// the tile).  ids holds table entries [chunk0, chunk0 + 64) in lane order.
+template <int D, int B, bool kMasked>
+__device__ __forceinline__ void tile_step(LaneState& st, const TileCtx& c, int t0, int ids,
+                                          int chunk0)
+{
+    using G = Geometry<D, B>;
+    u32x4 kr[kLoads], vr[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const int tj = t0 + j * G::kTokensPerLoad;  // first token of this load (uniform)
+        if (!kMasked || tj < c.end) {
+            const int pb = readlane(ids, tj / B - chunk0);
+            const int64_t e = (int64_t)pb * c.block_elems + (int64_t)((tj % B) * c.token_stride) +
+                              c.lane_elem;
+            kr[j] = *reinterpret_cast<const u32x4*>(c.k + e);
+            vr[j] = *reinterpret_cast<const u32x4*>(c.v + e);
+        } else {
+            kr[j] = u32x4{0, 0, 0, 0};
+            vr[j] = u32x4{0, 0, 0, 0};
+        }
+    }
+    float x[kLoads];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        float d = __builtin_amdgcn_fdot2(as_h2(kr[j].x), c.q[0], 0.0f, false);
+        d = __builtin_amdgcn_fdot2(as_h2(kr[j].y), c.q[1], d, false);
+        d = __builtin_amdgcn_fdot2(as_h2(kr[j].z), c.q[2], d, false);
+        d = __builtin_amdgcn_fdot2(as_h2(kr[j].w), c.q[3], d, false);
+        d = group_sum<G::kLanesPerToken>(d) * c.scale_log2;
+        if (kMasked) {
+            const bool valid = t0 + j * G::kTokensPerLoad + c.group < c.end;
+            d = valid ? d : kNegInf;
+            vr[j] = valid ? vr[j] : u32x4{0, 0, 0, 0};
+        }
+        x[j] = d;
+        tmax = fmaxf(tmax, d);
+    }
+    const float m_new = fmaxf(st.m, tmax);
+    const float m_ref = m_new == kNegInf ? 0.0f : m_new;  // all masked so far: keep zeros
+    const float alpha = exp2_fast(st.m - m_ref);
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        st.acc[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        const float p = exp2_fast(x[j] - m_ref);
+        st.l += p;
+        const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const h2 v2 = as_h2(w[i]);
+            st.acc[2 * i] = fmaf(p, (float)v2.x, st.acc[2 * i]);
+            st.acc[2 * i + 1] = fmaf(p, (float)v2.y, st.acc[2 * i + 1]);
+        }
+    }
+    st.m = m_new;
+}
+
+// Merge (m, l, acc) of two partial softmax states with the log-sum-exp rule.
+__device__ __forceinline__ void merge_into(LaneState& st, float m_o, float l_o, const float* acc_o)
+{
+    const float M = fmaxf(st.m, m_o);
+    const float Mr = M == kNegInf ? 0.0f : M;
+    const float wa = exp2_fast(st.m - Mr), wb = exp2_fast(m_o - Mr);
+    st.l = st.l * wa + l_o * wb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        st.acc[i] = st.acc[i] * wa + acc_o[i] * wb;
+    st.m = M;
+}
+
+template <int D, int B>
+__global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
+{
+    using G = Geometry<D, B>;
+    constexpr int LPT = G::kLanesPerToken;
+    constexpr int TILE = G::kTile;
+
+    const uint32_t logical = xcd_remap(blockIdx.x, P.total_units);
+    const int part = (int)(logical % (uint32_t)P.num_partitions);
+    const uint32_t rest = logical / (uint32_t)P.num_partitions;
+    const int s = (int)(rest % (uint32_t)P.num_seqs);
+    const int h = (int)(rest / (uint32_t)P.num_seqs);
+
+    const int ctx = P.context_lens[s];
+    const int p0 = part * P.partition_size;
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int64_t row = ((int64_t)s * P.num_heads + h) * D;
+
+    if (ctx <= 0) {  // empty context: zero row, written by partition 0 only
+        if (part == 0 && threadIdx.x < D)
+            P.out[row + threadIdx.x] = (_Float16)0.0f;
+        return;
+    }
+    if (p0 >= ctx)
+        return;
+    const int end = min(p0 + P.partition_size, ctx);
+    const int nparts_seq = (ctx + P.partition_size - 1) / P.partition_size;
+
+    TileCtx c;
+    c.k = P.k_cache;
+    c.v = P.v_cache;
+    c.block_elems = (int64_t)B * P.num_heads * D;
+    c.group = lane / LPT;
+    c.token_stride = P.num_heads * D;
+    c.lane_elem = (c.group * P.num_heads + h) * D + (lane % LPT) * 8;
+    c.end = end;
+    c.scale_log2 = P.scale_log2;
+    {
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(P.q + row + (lane % LPT) * 8);
+        c.q[0] = as_h2(qv.x);
+        c.q[1] = as_h2(qv.y);
+        c.q[2] = as_h2(qv.z);
+        c.q[3] = as_h2(qv.w);
+    }
+
+    LaneState st;
+    st.m = kNegInf;
+    st.l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        st.acc[i] = 0.0f;
+
+    const int32_t* table = P.block_tables + (int64_t)s * P.max_blocks_per_seq;
+    const int first_blk = p0 / B;
+    const int last_blk = (end + B - 1) / B;  // exclusive
+    // Chunks of 64 table entries; a chunk spans 64*B tokens = whole tiles.
+    for (int chunk0 = first_blk; chunk0 < last_blk; chunk0 += kWave) {
+        const int n_ids = min(kWave, last_blk - chunk0);
+        const int ids = lane < n_ids ? table[chunk0 + lane] : 0;
+        const int tok_lo = chunk0 * B;
+        const int tok_hi = min(end, (chunk0 + kWave) * B);
+        for (int t0 = tok_lo + wave * TILE; t0 < tok_hi; t0 += kWaves * TILE) {
+            if (t0 + TILE <= end)
+                tile_step<D, B, false>(st, c, t0, ids, chunk0);
+            else
+                tile_step<D, B, true>(st, c, t0, ids, chunk0);
+        }
+    }
+
+    // Merge the lane groups of this wave (lanes l, l^LPT, l^2LPT, ...).
+#pragma unroll
+    for (int off = LPT; off < kWave; off <<= 1) {
+        float acc_o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc_o[i] = __shfl_xor(st.acc[i], off);
+        const float m_o = __shfl_xor(st.m, off);
+        const float l_o = __shfl_xor(st.l, off);
+        merge_into(st, m_o, l_o, acc_o);
+    }
+
+    // Merge the waves through LDS in wave order.
+    __shared__ float s_acc[kWaves][D];
+    __shared__ float s_m[kWaves], s_l[kWaves];
+    if (lane < LPT) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            s_acc[wave][lane * 8 + i] = st.acc[i];
+    }
+    if (lane == 0) {
+        s_m[wave] = st.m;
+        s_l[wave] = st.l;
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        float M = s_m[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            M = fmaxf(M, s_m[w]);
+        float L = 0.0f, o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float wt = s_m[w] == kNegInf ? 0.0f : exp2_fast(s_m[w] - M);
+            L = fmaf(s_l[w], wt, L);
+            o = fmaf(s_acc[w][d], wt, o);
+        }
+        o = o / L;
+        if (nparts_seq == 1) {
+            P.out[row + d] = (_Float16)o;
+        } else {
+            const int64_t u = ((int64_t)s * P.num_heads + h) * P.num_partitions + part;
+            P.ws_o[u * D + d] = o;
+            if (d == 0) {
+                P.ws_m[u] = M;
+                P.ws_l[u] = L;
+            }
+        }
+    }
+}
+
+// Merge the partitions of one (sequence, head): M = max m_p,
+// w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p.
+template <int D>
+__global__ __launch_bounds__(kWave) void pa_reduce_kernel(DecodeParams P)
+{
+    constexpr int kCols = D / kWave;  // columns per lane
+    const int sh = blockIdx.x;
+    const int s = sh / P.num_heads;
+    const int ctx = P.context_lens[s];
+    const int np = (ctx + P.partition_size - 1) / P.partition_size;
+    if (np <= 1)
+        return;
+    const int lane = threadIdx.x;
+    const int64_t u0 = (int64_t)sh * P.num_partitions;
+    const float* m = P.ws_m + u0;
+    const float* l = P.ws_l + u0;
+    const float* o = P.ws_o + u0 * D;
+
+    float M = kNegInf;
+    for (int p = lane; p < np; p += kWave)
+        M = fmaxf(M, m[p]);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1)
+        M = fmaxf(M, __shfl_xor(M, off));
+
+    float acc[kCols];
+#pragma unroll
+    for (int i = 0; i < kCols; ++i)
+        acc[i] = 0.0f;
+    float L = 0.0f;
+    for (int c0 = 0; c0 < np; c0 += kWave) {
+        const int n = min(kWave, np - c0);
+        const float w = lane < n ? l[c0 + lane] * exp2_fast(m[c0 + lane] - M) : 0.0f;
+        for (int j = 0; j < n; ++j) {
+            const float wj = readlane_f(w, j);
+            L += wj;
+            const float* oj = o + (int64_t)(c0 + j) * D + lane * kCols;
+#pragma unroll
+            for (int i = 0; i < kCols; ++i)
+                acc[i] = fmaf(wj, oj[i], acc[i]);
+        }
+    }
+    _Float16* out = P.out + (int64_t)sh * D + lane * kCols;
+#pragma unroll
+    for (int i = 0; i < kCols; ++i)
+        out[i] = (_Float16)(acc[i] / L);
+}
+
+template <int D, int B>
+hipError_t launch_decode(const DecodeParams& P, hipStream_t stream)
+{
+    hipLaunchKernelGGL((pa_partition_kernel<D, B>), dim3(P.total_units), dim3(kThreads), 0,
+                       stream, P);
+    if (P.num_partitions > 1)
+        hipLaunchKernelGGL((pa_reduce_kernel<D>), dim3(P.num_seqs * P.num_heads), dim3(kWave), 0,
+                           stream, P);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_dispatch(const DecodeParams& P, int head_dim, int block_size,
+                                  hipStream_t stream)
+{
+    if (head_dim == 128 && block_size == 16)
+        return launch_decode<128, 16>(P, stream);
+    if (head_dim == 128 && block_size == 32)
+        return launch_decode<128, 32>(P, stream);
+    if (head_dim == 64 && block_size == 16)
+        return launch_decode<64, 16>(P, stream);
+    if (head_dim == 64 && block_size == 32)
+        return launch_decode<64, 32>(P, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pa

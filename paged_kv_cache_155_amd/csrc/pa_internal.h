@@ -1,0 +1,38 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#ifndef PA_INTERNAL_H_
+#define PA_INTERNAL_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeParams {
+    _Float16* out;
+    const _Float16* q;
+    const _Float16* k_cache;
+    const _Float16* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* ws_o;  // [S, H, NP, D] normalised partition rows
+    float* ws_m;  // [S, H, NP] partition maxima (base-2 logits)
+    float* ws_l;  // [S, H, NP] partition sums
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t max_blocks_per_seq;
+    int32_t partition_size;  // tokens per partition (the whole table when not split)
+    int32_t num_partitions;  // NP = ceil(max_blocks_per_seq * block_size / partition_size)
+    uint32_t total_units;    // num_seqs * num_heads * num_partitions workgroups
+    float scale_log2;        // scale * log2(e)
+};
+
+hipError_t launch_decode_dispatch(const DecodeParams& p, int head_dim, int block_size,
+                                  hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                    void* v_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                                    int64_t num_slots, int32_t row_vectors, hipStream_t stream);
+
+}  // namespace pa
+
+#endif  // PA_INTERNAL_H_

@@ -276,3 +276,56 @@ def make_workload(config, block_size=None, num_seqs=None, num_heads=None, varian
         q=q, k_cache=k_cache, v_cache=v_cache, block_tables=tables,
         context_lens=lens.astype(np.int32), key=key, value=value, slot_mapping=slots,
         poison_block=poison_block, ref_counts=ref)
+
+
+def make_random(context_lens, num_heads, head_dim, block_size, seed=0, partition_size=512,
+                max_blocks_per_seq=None, spare_blocks=3, poison=True):
+    """A custom-shaped workload for edge cases: the given context lengths,
+    scattered tables from a seeded permutation, N(0,1) fp16 data, one new
+    token per sequence with ctx > 0 (written at position ctx-1; sequences
+    with ctx == 0 get slot -1, i.e. no write)."""
+    lens = np.asarray(context_lens, dtype=np.int64)
+    S, H, D, B = len(lens), int(num_heads), int(head_dim), int(block_size)
+    ss = np.random.SeedSequence([SEED, 1000, seed])
+    st = dict(zip(["table", "q", "k", "v", "newk", "newv"], ss.spawn(6)))
+    nblk = [-(-int(L) // B) for L in lens]
+    MB = max(1, max(nblk, default=1)) if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    NB = sum(nblk) + 1 + int(spare_blocks)
+    perm = _gen(st["table"]).permutation(NB).astype(np.int64)
+    poison_block = int(perm[-1])
+    tables = np.full((S, MB), poison_block, dtype=np.int32)
+    c = 0
+    for s, n in enumerate(nblk):
+        tables[s, :n] = perm[c:c + n]
+        c += n
+    ref = np.zeros(NB, dtype=np.int32)
+    for s, n in enumerate(nblk):
+        np.add.at(ref, tables[s, :n].astype(np.int64), 1)
+    q = _normal_f16(st["q"], (S, H, D))
+    k_cache = _normal_f16(st["k"], (NB, B, H, D))
+    v_cache = _normal_f16(st["v"], (NB, B, H, D))
+    key = _normal_f16(st["newk"], (S, H, D))
+    value = _normal_f16(st["newv"], (S, H, D))
+    slots = np.full(S, -1, dtype=np.int64)
+    for s in range(S):
+        if lens[s] > 0:
+            p = int(lens[s]) - 1
+            slots[s] = int(tables[s, p // B]) * B + p % B
+    if poison:
+        nan = np.float16(np.nan)
+        k_cache[poison_block] = nan
+        v_cache[poison_block] = nan
+        for s in range(S):
+            L = int(lens[s])
+            if L % B:
+                k_cache[tables[s, (L - 1) // B], L % B:] = nan
+                v_cache[tables[s, (L - 1) // B], L % B:] = nan
+        ok = slots >= 0
+        k_cache.reshape(NB * B, H, D)[slots[ok]] = nan
+        v_cache.reshape(NB * B, H, D)[slots[ok]] = nan
+    return Workload(
+        name="random", config=-1, num_seqs=S, num_heads=H, head_dim=D, block_size=B,
+        num_blocks=NB, max_blocks_per_seq=MB, partition_size=int(partition_size),
+        scale=np.float32(1.0 / math.sqrt(D)), q=q, k_cache=k_cache, v_cache=v_cache,
+        block_tables=tables, context_lens=lens.astype(np.int32), key=key, value=value,
+        slot_mapping=slots, poison_block=poison_block, ref_counts=ref)

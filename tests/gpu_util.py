@@ -1,0 +1,70 @@
+"""Shared helpers of the GPU tests: upload a workload, run the HIP path
+through the C ABI binding, run the oracle on the same host bytes, compare."""
+import sys
+
+import numpy as np
+
+# fp16 inputs, fp32 accumulation: |gpu - oracle| <= ATOL + RTOL * |oracle|
+ATOL = 2e-3
+RTOL = 1e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dev="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+class DeviceWorkload:
+    """The device copies of one Workload's arrays."""
+
+    def __init__(self, w, dev="cuda"):
+        import torch
+        self.w = w
+        self.q = to_dev(w.q, dev)
+        self.k_cache = to_dev(w.k_cache, dev)
+        self.v_cache = to_dev(w.v_cache, dev)
+        self.block_tables = to_dev(w.block_tables, dev)
+        self.context_lens = to_dev(w.context_lens, dev)
+        self.key = to_dev(w.key, dev)
+        self.value = to_dev(w.value, dev)
+        self.slot_mapping = to_dev(w.slot_mapping, dev)
+        self.out = torch.full_like(self.q, float("nan"))
+
+    def reshape_and_cache(self):
+        import paged_kv_cache_155_amd as pa
+        pa.reshape_and_cache(self.key, self.value, self.k_cache, self.v_cache, self.slot_mapping)
+
+    def decode(self, partition_size=None, out=None, workspace=None):
+        import paged_kv_cache_155_amd as pa
+        P = self.w.partition_size if partition_size is None else partition_size
+        o = self.out if out is None else out
+        pa.decode(o, self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
+                  float(self.w.scale), partition_size=P, workspace=workspace)
+        return o
+
+
+def oracle_after_write(orc, w):
+    """Host pools after the oracle's reshape_and_cache, and the oracle decode."""
+    kc = w.k_cache.copy()
+    vc = w.v_cache.copy()
+    orc.reshape_and_cache(w.key, w.value, kc, vc, w.slot_mapping)
+    ref = orc.decode(w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale))
+    return kc, vc, ref
+
+
+def assert_close(got_f16, ref, what=""):
+    got = got_f16.astype(np.float64)
+    err = np.abs(got - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    bad = ~(err <= bound)  # NaN counts as bad
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} outside {ATOL}+{RTOL}|ref|; first {idx.tolist()}"
+            f" got {got[tuple(idx[0])]} ref {ref[tuple(idx[0])]}")
+    return float(err.max()), float((err / np.maximum(np.abs(ref), 1e-30)).max())
