@@ -42,8 +42,10 @@ def _args():
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=float, default=2.0e6,
-                    help="token-heads of oracle work in the CPU baseline sample")
+    ap.add_argument("--cpu-sample-tokens", type=float, default=1.0e7,
+                    help="cap on token-heads of oracle work in the CPU baseline sample")
+    ap.add_argument("--cpu-repeats", type=int, default=3,
+                    help="oracle runs over the sample (the median is reported)")
     ap.add_argument("--probe", choices=["copy"], default=None)
     ap.add_argument("--probe-mib", type=int, default=1024)
     return ap.parse_args()
@@ -89,10 +91,10 @@ def probe_copy(mib):
                       "write_bytes_per_launch": 2 * T * row}), flush=True)
 
 
-def cpu_baseline(w, sample_tokens):
+def cpu_baseline(w, sample_tokens, repeats):
     """Time the oracle (as it stands) on a bounded, deterministic sample of
-    (sequence, head) pairs of the same workload; GB/s over the sampled
-    K/V bytes."""
+    (sequence, head) pairs of the same workload (the whole workload when it
+    is under the cap); GB/s over the sampled K/V bytes, median of repeats."""
     import numpy as np
     import oracle
     from paged_kv_cache_155_amd.workloads import kv_bytes_per_token
@@ -110,16 +112,19 @@ def cpu_baseline(w, sample_tokens):
         s, h = pairs[i]
         chosen.append((s, h))
         tok += int(w.context_lens[s])
-    t0 = time.perf_counter()
-    orc.decode_pairs(chosen, w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale))
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(max(1, repeats)):
+        t0 = time.perf_counter()
+        orc.decode_pairs(chosen, w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale))
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     nbytes = tok * kv_bytes_per_token(1, w.head_dim)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": orc.threads_used,
             "kind": "oracle",
-            "sample": f"{len(chosen)} of {len(pairs)} (sequence, head) pairs drawn with a seeded "
-                      f"permutation, {tok} token-heads, one fp64 oracle decode; "
-                      f"{dt:.2f} s wall, tokens/s/layer-equivalent "
-                      f"{len(chosen) / H / dt:.1f}"}
+            "sample": f"{len(chosen)} of {len(pairs)} (sequence, head) pairs (seeded permutation), "
+                      f"{tok} token-heads = {nbytes} K/V bytes; fp64 oracle decode, median of "
+                      f"{len(times)} runs = {dt:.3f} s wall on {orc.threads_used} threads; "
+                      f"tokens/s/layer-equivalent {len(chosen) / H / dt:.1f}"}
 
 
 def main():
@@ -218,7 +223,7 @@ def main():
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens)
+        line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens, a.cpu_repeats)
     print(json.dumps(line), flush=True)
 
 

@@ -13,10 +13,14 @@
 // Design on CDNA4 (decode with one query per head is a batched GEMV: every
 // K/V byte is used once, so the bound is HBM bandwidth and MFMA has nothing
 // to do):
-//   * one workgroup (4 waves) per (sequence, head, context partition); the
-//     hardware workgroup id is remapped so that each of the 8 XCDs, which
-//     receive workgroups round-robin, gets a contiguous range of heads
-//     (physical blocks shared between sequences then meet in one L2);
+//   * one workgroup (4 waves) per (sequence, head, context partition).  The
+//     logical unit order is sequence fastest, then partition, then head, and
+//     the hardware workgroup id is remapped so that each of the 8 XCDs (which
+//     receive workgroups round-robin) gets a contiguous range of that order:
+//     an XCD works through whole heads, and the long and short partitions of
+//     a ragged batch are spread evenly over time;
+//   * K/V are streamed with nontemporal loads (read once, so they should not
+//     displace other lines in the caches);
 //   * a wave walks 32-token tiles (64 for head_dim 64).  For head_dim 128 a
 //     token's row of one head is 256 contiguous bytes = 16 lanes x 16 bytes,
 //     so one global_load_dwordx4 covers 4 tokens; a tile issues 8 K loads
@@ -139,8 +143,8 @@ __device__ __forceinline__ void tile_step(LaneState& st, const TileCtx& c, int t
             const int pb = readlane(ids, tj / B - chunk0);
             const int64_t e = (int64_t)pb * c.block_elems + (int64_t)((tj % B) * c.token_stride) +
                               c.lane_elem;
-            kr[j] = *reinterpret_cast<const u32x4*>(c.k + e);
-            vr[j] = *reinterpret_cast<const u32x4*>(c.v + e);
+            kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c.k + e));
+            vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c.v + e));
         } else {
             kr[j] = u32x4{0, 0, 0, 0};
             vr[j] = u32x4{0, 0, 0, 0};
@@ -206,10 +210,10 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
     constexpr int TILE = G::kTile;
 
     const uint32_t logical = xcd_remap(blockIdx.x, P.total_units);
-    const int part = (int)(logical % (uint32_t)P.num_partitions);
-    const uint32_t rest = logical / (uint32_t)P.num_partitions;
-    const int s = (int)(rest % (uint32_t)P.num_seqs);
-    const int h = (int)(rest / (uint32_t)P.num_seqs);
+    const int s = (int)(logical % (uint32_t)P.num_seqs);
+    const uint32_t rest = logical / (uint32_t)P.num_seqs;
+    const int part = (int)(rest % (uint32_t)P.num_partitions);
+    const int h = (int)(rest / (uint32_t)P.num_partitions);
 
     const int ctx = P.context_lens[s];
     const int p0 = part * P.partition_size;
