@@ -325,51 +325,75 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
 }
 
 // Merge the partitions of one (sequence, head): M = max m_p,
-// w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p.
+// w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p.  A workgroup of
+// 256 threads per (sequence, head): thread (g, d) sums column d over the
+// partitions p = g, g + G, ... (G = 256 / D groups), the groups are then
+// added in order g = 0, 1, ... - a fixed order, so the result is
+// deterministic.  Partitions are taken 256 at a time.
 template <int D>
-__global__ __launch_bounds__(kWave) void pa_reduce_kernel(DecodeParams P)
+__global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
 {
-    constexpr int kCols = D / kWave;  // columns per lane
+    constexpr int G = kThreads / D;
     const int sh = blockIdx.x;
     const int s = sh / P.num_heads;
     const int ctx = P.context_lens[s];
     const int np = (ctx + P.partition_size - 1) / P.partition_size;
     if (np <= 1)
         return;
-    const int lane = threadIdx.x;
+    const int t = threadIdx.x;
+    const int lane = t % kWave;
+    const int wave = t / kWave;
+    const int g = t / D;
+    const int d = t % D;
     const int64_t u0 = (int64_t)sh * P.num_partitions;
     const float* m = P.ws_m + u0;
     const float* l = P.ws_l + u0;
     const float* o = P.ws_o + u0 * D;
 
+    __shared__ float s_red[kWaves];
+    __shared__ float s_w[kThreads];
+    __shared__ float s_acc[G][D];
+
     float M = kNegInf;
-    for (int p = lane; p < np; p += kWave)
+    for (int p = t; p < np; p += kThreads)
         M = fmaxf(M, m[p]);
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1)
         M = fmaxf(M, __shfl_xor(M, off));
+    if (lane == 0)
+        s_red[wave] = M;
+    __syncthreads();
+    M = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        M = fmaxf(M, s_red[w]);
 
-    float acc[kCols];
-#pragma unroll
-    for (int i = 0; i < kCols; ++i)
-        acc[i] = 0.0f;
-    float L = 0.0f;
-    for (int c0 = 0; c0 < np; c0 += kWave) {
-        const int n = min(kWave, np - c0);
-        const float w = lane < n ? l[c0 + lane] * exp2_fast(m[c0 + lane] - M) : 0.0f;
-        for (int j = 0; j < n; ++j) {
-            const float wj = readlane_f(w, j);
-            L += wj;
-            const float* oj = o + (int64_t)(c0 + j) * D + lane * kCols;
-#pragma unroll
-            for (int i = 0; i < kCols; ++i)
-                acc[i] = fmaf(wj, oj[i], acc[i]);
-        }
+    float acc = 0.0f, L = 0.0f;
+    for (int c0 = 0; c0 < np; c0 += kThreads) {
+        const int n = min(kThreads, np - c0);
+        __syncthreads();  // s_w of the previous chunk fully consumed
+        if (t < n)
+            s_w[t] = l[c0 + t] * exp2_fast(m[c0 + t] - M);
+        __syncthreads();
+        const float* oc = o + (int64_t)c0 * D + d;
+#pragma unroll 8
+        for (int p = g; p < n; p += G)
+            acc = fmaf(s_w[p], oc[(int64_t)p * D], acc);
+        if (t == 0)
+            for (int p = 0; p < n; ++p)
+                L += s_w[p];
     }
-    _Float16* out = P.out + (int64_t)sh * D + lane * kCols;
+    s_acc[g][d] = acc;
+    if (t == 0)
+        s_red[0] = L;
+    __syncthreads();
+    if (t < D) {
+        float sum = s_acc[0][t];
 #pragma unroll
-    for (int i = 0; i < kCols; ++i)
-        out[i] = (_Float16)(acc[i] / L);
+        for (int gg = 1; gg < G; ++gg)
+            sum += s_acc[gg][t];
+        P.out[(int64_t)sh * D + t] = (_Float16)(sum / s_red[0]);
+    }
 }
 
 template <int D, int B>
@@ -378,8 +402,8 @@ hipError_t launch_decode(const DecodeParams& P, hipStream_t stream)
     hipLaunchKernelGGL((pa_partition_kernel<D, B>), dim3(P.total_units), dim3(kThreads), 0,
                        stream, P);
     if (P.num_partitions > 1)
-        hipLaunchKernelGGL((pa_reduce_kernel<D>), dim3(P.num_seqs * P.num_heads), dim3(kWave), 0,
-                           stream, P);
+        hipLaunchKernelGGL((pa_reduce_kernel<D>), dim3(P.num_seqs * P.num_heads), dim3(kThreads),
+                           0, stream, P);
     return hipGetLastError();
 }
 
