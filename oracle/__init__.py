@@ -51,6 +51,10 @@ class Oracle:
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_reshape_and_cache.argtypes = [_P] * 5 + [_I32] * 5
         lib.oracle_reshape_and_cache.restype = ctypes.c_int
+        lib.oracle_copy_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I64]
+        lib.oracle_copy_blocks.restype = ctypes.c_int
+        lib.oracle_swap_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I64]
+        lib.oracle_swap_blocks.restype = ctypes.c_int
         self.lib = lib
         self.threads_used = 1
 
@@ -129,6 +133,32 @@ class Oracle:
                                                _ptr(sm), T, H, D, nb, bs)
         if rc:
             raise ValueError(f"oracle_reshape_and_cache failed ({rc})")
+
+    # -- block copies -----------------------------------------------------------
+    def copy_blocks(self, k_cache, v_cache, block_mapping):
+        """In place: block dst of both caches becomes a copy of block src, for
+        each (src, dst) row of block_mapping [N, 2]."""
+        kc = k_cache.view(np.uint16) if k_cache.dtype == np.float16 else k_cache
+        vc = v_cache.view(np.uint16) if v_cache.dtype == np.float16 else v_cache
+        assert kc.flags.c_contiguous and vc.flags.c_contiguous and kc.shape == vc.shape
+        m = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2))
+        nb = kc.shape[0]
+        rc = self.lib.oracle_copy_blocks(_ptr(kc), _ptr(vc), _ptr(m), m.shape[0], nb,
+                                         int(np.prod(kc.shape[1:])))
+        if rc:
+            raise ValueError(f"oracle_copy_blocks failed ({rc})")
+
+    def swap_blocks(self, src, dst, block_mapping):
+        """In place on dst: block b of dst becomes a copy of block a of src for
+        each (a, b) row of block_mapping [N, 2]."""
+        s_ = _u16(src)
+        d_ = dst.view(np.uint16) if dst.dtype == np.float16 else dst
+        assert d_.flags.c_contiguous and s_.shape[1:] == d_.shape[1:]
+        m = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2))
+        rc = self.lib.oracle_swap_blocks(_ptr(s_), _ptr(d_), _ptr(m), m.shape[0], s_.shape[0],
+                                         d_.shape[0], int(np.prod(s_.shape[1:])))
+        if rc:
+            raise ValueError(f"oracle_swap_blocks failed ({rc})")
 
 
 _default = None

@@ -18,6 +18,11 @@
  *   [eng]  "深入解析LLM推理引擎：从PagedAttention到调度优化"
  *          §3.2  block table worked example (block size 4, table [0, 1, 3, ...])
  *          §3.3  the gather is driven by block_table and current_position
+ *   [arch] "vLLM基础架构：核心组件、PagedAttention原理、KV Cache管理与连续批处理机制"
+ *          §2.3  shared blocks are copied before a sequence writes into one
+ *                (copy-on-write), then its table points at the copy
+ *   [src]  "【硬核】啃透vLLM源码：从PagedAttention到连续批处理，大模型推理加速24倍的秘密"
+ *          §三   blocks are swapped out to host memory and back in
  *
  * Arithmetic: every fp16 value is decoded exactly to double (IEEE-754
  * binary16 definition, written out below) and all arithmetic is in double.
@@ -293,6 +298,56 @@ int oracle_reshape_and_cache(const uint16_t *key, const uint16_t *value,
                 k_cache[dst] = key[src];
                 v_cache[dst] = value[src];
             }
+    }
+    return OR_OK;
+}
+
+/*
+ * Copy whole physical blocks inside a cache pair ([arch] §2.3 copy-on-write):
+ * for each pair i, block mapping[2i+1] of k_cache and v_cache becomes a
+ * bitwise copy of block mapping[2i].  block_elems = block_size * num_heads *
+ * head_dim.  Pairs naming a block outside [0, num_blocks) are skipped.
+ * Destinations are distinct and no destination is also a source in the same
+ * call; under that precondition the pair order does not matter.
+ */
+int oracle_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int64_t *mapping,
+                       int32_t num_pairs, int32_t num_blocks, int64_t block_elems)
+{
+    if (num_pairs < 0 || num_blocks <= 0 || block_elems <= 0)
+        return OR_ERR_ARG;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        int64_t src = mapping[2 * i], dst = mapping[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks)
+            continue;
+        for (int64_t e = 0; e < block_elems; ++e) {
+            k_cache[dst * block_elems + e] = k_cache[src * block_elems + e];
+            v_cache[dst * block_elems + e] = v_cache[src * block_elems + e];
+        }
+    }
+    return OR_OK;
+}
+
+/*
+ * Move whole blocks between two caches of the same block shape ([src] §三:
+ * swap out to host memory, swap back in): for each pair i, block
+ * mapping[2i+1] of dst becomes a bitwise copy of block mapping[2i] of src.
+ * Pairs outside [0, src_blocks) x [0, dst_blocks) are rejected.
+ */
+int oracle_swap_blocks(const uint16_t *src, uint16_t *dst, const int64_t *mapping,
+                       int32_t num_pairs, int32_t src_blocks, int32_t dst_blocks,
+                       int64_t block_elems)
+{
+    if (num_pairs < 0 || src_blocks <= 0 || dst_blocks <= 0 || block_elems <= 0)
+        return OR_ERR_ARG;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        int64_t a = mapping[2 * i], b = mapping[2 * i + 1];
+        if (a < 0 || a >= src_blocks || b < 0 || b >= dst_blocks)
+            return OR_ERR_RANGE;
+    }
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        int64_t a = mapping[2 * i], b = mapping[2 * i + 1];
+        for (int64_t e = 0; e < block_elems; ++e)
+            dst[b * block_elems + e] = src[a * block_elems + e];
     }
     return OR_OK;
 }

@@ -19,6 +19,9 @@ What pins what:
   paging           bitwise invariance under relabelling of physical blocks
   reshape_and_cache  numpy scatter by slot on sentinel pools, special bit
                    patterns, out-of-range slots, the worked example's slot
+  copy / swap      numpy block assignment on random bit patterns; a
+                   copy-on-write sequence ("vLLM基础架构" §2.3) seen through
+                   the gather; out-of-range pairs
 """
 import json
 import math
@@ -295,9 +298,83 @@ def pin_reshape_worked_example(orc):
     assert not K[:pos].any()
 
 
+def _rand_bits(rng, shape):
+    a = rng.integers(0, 1 << 16, size=shape, dtype=np.uint32).astype(np.uint16)
+    a.reshape(-1)[:len(_SPECIAL)] = _SPECIAL
+    return a
+
+
+def pin_copy_blocks(orc):
+    rng = np.random.default_rng(8)
+    NB, B, H, D = 12, 16, 3, 64
+    kc0 = _rand_bits(rng, (NB, B, H, D))
+    vc0 = _rand_bits(rng, (NB, B, H, D))
+    perm = rng.permutation(NB)
+    mapping = np.stack([perm[:4], perm[4:8]], axis=1).astype(np.int64)  # 4 src -> 4 fresh dst
+    bad = np.array([[-1, perm[8]], [perm[0], NB]], dtype=np.int64)       # skipped
+    kc, vc = kc0.copy(), vc0.copy()
+    orc.copy_blocks(kc, vc, np.concatenate([mapping, bad]))
+    rk, rv = kc0.copy(), vc0.copy()
+    rk[mapping[:, 1]] = kc0[mapping[:, 0]]
+    rv[mapping[:, 1]] = vc0[mapping[:, 0]]
+    assert np.array_equal(kc, rk) and np.array_equal(vc, rv)
+
+
+def pin_copy_on_write(orc):
+    """Two sequences share block X; the second must write into it, so X is
+    copied to a free block Y, its table points at Y, and the write lands in
+    Y: the first sequence still reads the old data, the second the new."""
+    B, H, D = 4, 1, 2
+    NB = 4
+    kc = np.zeros((NB, B, H, D), dtype=np.float16)
+    for b in range(NB):
+        for o in range(B):
+            kc[b, o, 0] = (b, o)
+    vc = -kc
+    X, Y = 2, 3
+    tables = np.array([[0, X], [1, X]], dtype=np.int32)
+    orc.copy_blocks(kc, vc, [[X, Y]])
+    tables[1, 1] = Y
+    pos = 6                       # logical block 1, offset 2
+    slot = int(tables[1, pos // B]) * B + pos % B
+    orc.reshape_and_cache(np.array([[[50.0, 60.0]]], np.float16),
+                          np.array([[[-50.0, -60.0]]], np.float16), kc, vc,
+                          np.array([slot], dtype=np.int64))
+    lens = np.array([8, 8], dtype=np.int32)
+    K0, _ = orc.gather(kc, vc, tables, lens, 0, 0)
+    K1, V1 = orc.gather(kc, vc, tables, lens, 1, 0)
+    assert np.array_equal(K0[4:8], [[X, 0], [X, 1], [X, 2], [X, 3]])
+    assert np.array_equal(K1[4:8], [[X, 0], [X, 1], [50, 60], [X, 3]])
+    assert np.array_equal(V1[pos], [-50, -60])
+
+
+def pin_swap_blocks(orc):
+    rng = np.random.default_rng(9)
+    shape = (3, 16, 2, 128)
+    gpu = _rand_bits(rng, (10,) + shape[1:])
+    host = np.zeros((6,) + shape[1:], dtype=np.uint16)
+    out_map = np.array([[7, 0], [2, 5], [9, 3]], dtype=np.int64)
+    orc.swap_blocks(gpu, host, out_map)
+    ref = np.zeros_like(host)
+    ref[out_map[:, 1]] = gpu[out_map[:, 0]]
+    assert np.array_equal(host, ref)
+    back = np.zeros_like(gpu)
+    in_map = out_map[:, ::-1].copy()
+    in_map[:, 1] = [1, 4, 8]
+    orc.swap_blocks(host, back, in_map)
+    assert np.array_equal(back[[1, 4, 8]], gpu[[7, 2, 9]])
+    try:
+        orc.swap_blocks(gpu, host, [[0, 6]])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("out-of-range swap accepted")
+
+
 PINS = [pin_half_decode_exhaustive, pin_gather_worked_example, pin_contiguous_sdpa,
         pin_block_permutation_invariance, pin_brute_force_tiny, pin_closed_forms, pin_needles,
-        pin_reshape_scatter, pin_reshape_worked_example]
+        pin_reshape_scatter, pin_reshape_worked_example, pin_copy_blocks, pin_copy_on_write,
+        pin_swap_blocks]
 
 
 def main(argv):

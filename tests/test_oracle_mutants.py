@@ -44,6 +44,12 @@ MUTANTS = {
     "reshape_block_mod": ("int64_t block = slot / block_size;", "int64_t block = slot % block_size;"),
     "reshape_no_upper_check": ("if (slot < 0 || slot >= num_slots)", "if (slot < 0)"),
     "reshape_value_gets_key": ("v_cache[dst] = value[src];", "v_cache[dst] = key[src];"),
+    "copy_direction": ("k_cache[dst * block_elems + e] = k_cache[src * block_elems + e];",
+                       "k_cache[src * block_elems + e] = k_cache[dst * block_elems + e];"),
+    "copy_skips_v": ("            v_cache[dst * block_elems + e] = v_cache[src * block_elems + e];\n", ""),
+    "swap_no_range_check": ("        if (a < 0 || a >= src_blocks || b < 0 || b >= dst_blocks)\n            return OR_ERR_RANGE;\n", ""),
+    "swap_uses_dst_index_for_src": ("dst[b * block_elems + e] = src[a * block_elems + e];",
+                                    "dst[b * block_elems + e] = src[b * block_elems + e];"),
 }
 
 
