@@ -46,6 +46,10 @@ def _args():
                     help="cap on token-heads of oracle work in the CPU baseline sample")
     ap.add_argument("--cpu-repeats", type=int, default=3,
                     help="oracle runs over the sample (the median is reported)")
+    ap.add_argument("--op", choices=["step", "copy_blocks", "swap"], default="step",
+                    help="step: the decode step (default); copy_blocks / swap: the block "
+                         "copy-on-write and GPU<->host swap entry points on config 1's pool")
+    ap.add_argument("--pairs", type=int, default=1024, help="blocks per copy/swap call")
     ap.add_argument("--probe", choices=["copy"], default=None)
     ap.add_argument("--probe-mib", type=int, default=1024)
     return ap.parse_args()
@@ -89,6 +93,78 @@ def probe_copy(mib):
     print(json.dumps({"probe": "copy", "kernel": "reshape_and_cache_kernel", "launches": 3,
                       "read_bytes_per_launch": 2 * T * row + 8 * T,
                       "write_bytes_per_launch": 2 * T * row}), flush=True)
+
+
+PCIE5_X16_GBS = 63.0  # 32 GT/s x 16 lanes x 128/130 / 8, one direction
+
+
+def _time_events(fn, iters, warmup=3):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def bench_blocks(op, pairs, iters):
+    """copy_blocks: `pairs` random (src -> fresh dst) block copies inside
+    config 1's K/V pool; swap: `pairs` blocks of K and of V out to pinned host
+    memory and back in.  One JSON line per measured direction."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import make_workload
+    w = make_workload(1, poison=False)
+    kc = torch.from_numpy(w.k_cache).cuda()
+    vc = torch.from_numpy(w.v_cache).cuda()
+    block_bytes = w.k_cache[0].nbytes
+    rng = np.random.default_rng(155)
+    perm = rng.permutation(w.num_blocks)
+    n = min(pairs, w.num_blocks // 2)
+    lines = []
+    if op == "copy_blocks":
+        mapping = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int64)).cuda()
+        ms = _time_events(lambda: pa.copy_blocks(kc, vc, mapping), iters)
+        moved = n * block_bytes * 2 * 2  # K and V, read + write
+        t = float(np.median(ms)) * 1e-3
+        lines.append({"op": "copy_blocks", "pairs": n, "block_bytes": block_bytes,
+                      "bytes_per_call": moved, "us_median": round(t * 1e6, 2),
+                      "roofline": {"bound": "hbm", "achieved": round(moved / t / 1e9, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(moved / t / 1e9 / HBM_PEAK_GBS, 4)}})
+    else:
+        hk = torch.empty((n,) + tuple(kc.shape[1:]), dtype=torch.float16).pin_memory()
+        hv = torch.empty_like(hk).pin_memory()
+        out_map = torch.from_numpy(np.stack([perm[:n], np.arange(n)], 1).astype(np.int64))
+        in_map = torch.from_numpy(np.stack([np.arange(n), perm[n:2 * n]], 1).astype(np.int64))
+
+        def out_():
+            pa.swap_blocks(kc, hk, out_map)
+            pa.swap_blocks(vc, hv, out_map)
+
+        def in_():
+            pa.swap_blocks(hk, kc, in_map)
+            pa.swap_blocks(hv, vc, in_map)
+
+        for name, fn in (("swap_out", out_), ("swap_in", in_)):
+            ms = _time_events(fn, iters)
+            moved = n * block_bytes * 2
+            t = float(np.median(ms)) * 1e-3
+            lines.append({"op": name, "pairs": n, "block_bytes": block_bytes,
+                          "bytes_per_call": moved, "us_median": round(t * 1e6, 2),
+                          "roofline": {"bound": "pcie", "achieved": round(moved / t / 1e9, 2),
+                                       "peak": PCIE5_X16_GBS, "unit": "GB/s",
+                                       "frac": round(moved / t / 1e9 / PCIE5_X16_GBS, 4)}})
+    for ln in lines:
+        print(json.dumps(ln), flush=True)
 
 
 def cpu_baseline(w, sample_tokens, repeats):
@@ -146,6 +222,9 @@ def main():
     pa.load()
     if a.probe == "copy":
         probe_copy(a.probe_mib)
+        return
+    if a.op != "step":
+        bench_blocks(a.op, a.pairs, a.steps)
         return
 
     w = make_workload(a.config, block_size=a.block_size, partition_size=a.partition_size,

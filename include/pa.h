@@ -11,12 +11,16 @@
  *          §3.2 on-demand block filling and the block table; §3.3 the gather
  *          driven by block_table and the current position
  *   [arch] "vLLM基础架构：核心组件、PagedAttention原理、KV Cache管理与连续批处理机制"
- *          §2.3 a new block every block_size tokens; shared prefix blocks
+ *          §2.3 a new block every block_size tokens; shared prefix blocks;
+ *          copy-on-write of a shared block before a sequence writes into it
+ *   [src]  "【硬核】啃透vLLM源码：从PagedAttention到连续批处理，大模型推理加速24倍的秘密"
+ *          §三 blocks swapped out to host memory and back in
  *
  * Conventions shared by every entry point
- *   - Every array pointer is a DEVICE pointer owned by the caller.  The
- *     library never allocates, frees or synchronises; it keeps no state
- *     between calls.  Work is enqueued on `stream` (a hipStream_t passed as
+ *   - Every array pointer is a DEVICE pointer owned by the caller, except
+ *     where an entry point says otherwise (pa_swap_blocks).  The library
+ *     never allocates, frees or synchronises; it keeps no state between
+ *     calls.  Work is enqueued on `stream` (a hipStream_t passed as
  *     void*, NULL = the null stream) and runs asynchronously in stream order.
  *   - fp16 means IEEE-754 binary16.  All arrays are dense, row-major, and
  *     their base pointers are 16-byte aligned.
@@ -47,7 +51,8 @@ enum {
     PA_ERR_PARTITION = -4,   /* partition_size not 0 and not a positive multiple of block_size */
     PA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than pa_decode_workspace_size */
     PA_ERR_ALIGN = -6,       /* a base pointer is not 16-byte aligned                */
-    PA_ERR_HIP = -7          /* the HIP runtime reported an error at launch          */
+    PA_ERR_HIP = -7,         /* the HIP runtime reported an error at launch          */
+    PA_ERR_RANGE = -8        /* a host-side block index is outside its cache          */
 };
 
 /*
@@ -128,6 +133,51 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
               int32_t max_blocks_per_seq, float scale, int32_t partition_size,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Copy whole physical blocks inside one cache pair: the copy-on-write step
+ * of [arch] §2.3 (a sequence about to write into a block it shares gets a
+ * private copy, and its table is then pointed at the copy by the caller).
+ * For each pair i, block block_mapping[2i+1] of k_cache and of v_cache
+ * becomes a bitwise copy of block block_mapping[2i].
+ *
+ *   k_cache,
+ *   v_cache        fp16 [num_blocks, block_size, num_heads, head_dim]
+ *   block_mapping  int64 [num_pairs, 2], DEVICE array of (src, dst) block ids.
+ *                  A pair naming a block outside [0, num_blocks) is skipped.
+ *                  Destinations must be distinct and no destination may be
+ *                  a source in the same call (otherwise the result is
+ *                  unspecified).
+ * Requires head_dim % 8 == 0.  num_pairs == 0 enqueues nothing.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int32_t num_pairs,
+                   int32_t num_blocks, int32_t block_size, int32_t num_heads, int32_t head_dim,
+                   void* stream);
+
+/*
+ * Move whole blocks between two caches of the same block shape, one of
+ * which may live in host memory: the swap-out / swap-in of [src] §三.  For
+ * each pair i, block block_mapping[2i+1] of dst becomes a bitwise copy of
+ * block block_mapping[2i] of src.
+ *
+ *   src, dst        base pointers of two caches ([src_num_blocks, ...] and
+ *                   [dst_num_blocks, ...] blocks), device memory or host
+ *                   memory.  src and dst must not overlap.
+ *   block_mapping   int64 [num_pairs, 2], HOST array of (src, dst) block ids;
+ *                   every id is range-checked first (PA_ERR_RANGE, nothing
+ *                   enqueued).
+ *   block_bytes     bytes of one block (block_size*num_heads*head_dim*2).
+ * When both caches are reachable from the GPU (device memory, or pinned host
+ * memory from hipHostMalloc, as hipPointerGetAttributes reports), the moves
+ * run as kernels on `stream` that read and write across PCIe (the pairs
+ * travel in the kernel arguments).  Otherwise they are hipMemcpyAsync copies
+ * on `stream`, with runs of pairs whose source and destination ids both
+ * increase by one merged into one copy (with pageable host memory these
+ * complete before the call returns).
+ */
+int pa_swap_blocks(const void* src, void* dst, const int64_t* block_mapping, int32_t num_pairs,
+                   int32_t src_num_blocks, int32_t dst_num_blocks, int64_t block_bytes,
+                   void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* pa_status_string(int status);

@@ -44,6 +44,10 @@ def load(path=None):
     lib.pa_decode.argtypes = ([_P] * 6 + [_I32] * 6 + [ctypes.c_float, _I32, _P, ctypes.c_size_t,
                                                        _P])
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_swap_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, ctypes.c_int64, _P]
+    lib.pa_swap_blocks.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -138,3 +142,46 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, partitio
     if rc != PA_OK:
         raise PAError(rc, "pa_decode")
     return out
+
+
+def copy_blocks(k_cache, v_cache, block_mapping, stream=None):
+    """Copy-on-write: for each (src, dst) row of block_mapping (int64 [N, 2] GPU
+    tensor), block dst of k_cache and v_cache ([NB, B, H, D] fp16) becomes a
+    bitwise copy of block src.  Enqueued on the current stream."""
+    import torch
+    _check(k_cache, "k_cache", torch.float16, ndim=4)
+    NB, B, H, D = k_cache.shape
+    _check(v_cache, "v_cache", torch.float16, shape=k_cache.shape)
+    _check(block_mapping, "block_mapping", torch.int64, ndim=2)
+    if block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [N, 2]")
+    rc = load().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
+                               block_mapping.shape[0], NB, B, H, D, _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_copy_blocks")
+
+
+def swap_blocks(src, dst, block_mapping, stream=None):
+    """Swap-out / swap-in: for each (a, b) row of block_mapping (int64 [N, 2]
+    CPU tensor), block b of dst becomes a copy of block a of src.  src and dst
+    are [NB, B, H, D] fp16 tensors with the same block shape, on the GPU or in
+    host memory.  With pinned host memory the move is one asynchronous kernel
+    on the current stream; pageable host memory falls back to copies that
+    complete before the call returns."""
+    import torch
+    for t, n in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_contiguous() \
+                or t.dim() != 4:
+            raise ValueError(f"{n} must be a contiguous fp16 [NB, B, H, D] tensor")
+    if tuple(src.shape[1:]) != tuple(dst.shape[1:]):
+        raise ValueError("src and dst must have the same block shape")
+    m = block_mapping
+    if not isinstance(m, torch.Tensor) or m.is_cuda or m.dtype != torch.int64 or m.dim() != 2 \
+            or m.shape[1] != 2:
+        raise ValueError("block_mapping must be a CPU int64 [N, 2] tensor")
+    m = m.contiguous()
+    block_bytes = src[0].numel() * 2
+    rc = load().pa_swap_blocks(_ptr(src), _ptr(dst), _ptr(m), m.shape[0], src.shape[0],
+                               dst.shape[0], block_bytes, _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_swap_blocks")

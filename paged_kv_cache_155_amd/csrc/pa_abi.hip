@@ -59,6 +59,7 @@ const char* pa_status_string(int status)
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a base pointer is not 16-byte aligned";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported a launch error";
+    case PA_ERR_RANGE: return "PA_ERR_RANGE: a block index is outside its cache";
     default: return "unknown pa status";
     }
 }
@@ -161,6 +162,50 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     }
     hipError_t e = pa::launch_decode_dispatch(p, head_dim, block_size,
                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int32_t num_pairs,
+                   int32_t num_blocks, int32_t block_size, int32_t num_heads, int32_t head_dim,
+                   void* stream)
+{
+    if (num_pairs < 0 || num_blocks <= 0 || block_size <= 0 || num_heads <= 0 || head_dim <= 0)
+        return PA_ERR_INVALID_DIM;
+    if (head_dim % 8 != 0)
+        return PA_ERR_UNSUPPORTED;
+    if (num_pairs == 0)
+        return PA_OK;
+    if (!k_cache || !v_cache || !block_mapping)
+        return PA_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(block_mapping) & 7u))
+        return PA_ERR_ALIGN;
+    const int64_t block_vecs = (int64_t)block_size * num_heads * head_dim / 8;
+    const int64_t chunks = (block_vecs + 2047) / 2048;
+    if ((int64_t)num_pairs * chunks > INT32_MAX)
+        return PA_ERR_INVALID_DIM;
+    hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_blocks,
+                                          block_vecs, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_swap_blocks(const void* src, void* dst, const int64_t* block_mapping, int32_t num_pairs,
+                   int32_t src_num_blocks, int32_t dst_num_blocks, int64_t block_bytes,
+                   void* stream)
+{
+    if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0 || block_bytes <= 0)
+        return PA_ERR_INVALID_DIM;
+    if (num_pairs == 0)
+        return PA_OK;
+    if (!src || !dst || !block_mapping)
+        return PA_ERR_NULL;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        const int64_t a = block_mapping[2 * i], b = block_mapping[2 * i + 1];
+        if (a < 0 || a >= src_num_blocks || b < 0 || b >= dst_num_blocks)
+            return PA_ERR_RANGE;
+    }
+    hipError_t e = pa::enqueue_swap_blocks(src, dst, block_mapping, num_pairs, block_bytes,
+                                           static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -33,6 +33,13 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     void* v_cache, const int64_t* slot_mapping, int32_t num_tokens,
                                     int64_t num_slots, int32_t row_vectors, hipStream_t stream);
 
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping,
+                              int32_t num_pairs, int64_t num_blocks, int64_t block_vecs,
+                              hipStream_t stream);
+
+hipError_t enqueue_swap_blocks(const void* src, void* dst, const int64_t* block_mapping,
+                               int32_t num_pairs, int64_t block_bytes, hipStream_t stream);
+
 }  // namespace pa
 
 #endif  // PA_INTERNAL_H_

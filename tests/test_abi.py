@@ -84,3 +84,21 @@ def test_reshape_rejects(lib):
     assert f(FAKE, P(0), FAKE, FAKE, FAKE, 3, 4, 128, 8, 16, None) == -1
     assert f(FAKE, FAKE, P(0x10004), FAKE, FAKE, 3, 4, 128, 8, 16, None) == -6
     assert f(P(0), P(0), P(0), P(0), P(0), 0, 4, 128, 8, 16, None) == 0
+
+
+def test_copy_and_swap_reject(lib):
+    import numpy as np
+    f = lib.pa_copy_blocks
+    assert f(FAKE, FAKE, FAKE, -1, 8, 16, 4, 128, None) == -2
+    assert f(FAKE, FAKE, FAKE, 2, 8, 16, 4, 12, None) == -3
+    assert f(FAKE, P(0), FAKE, 2, 8, 16, 4, 128, None) == -1
+    assert f(FAKE, FAKE, P(0x10004), 2, 8, 16, 4, 128, None) == -6
+    assert f(P(0), P(0), P(0), 0, 8, 16, 4, 128, None) == 0
+    g = lib.pa_swap_blocks
+    m = np.array([[0, 1], [2, 9]], dtype=np.int64)  # 9 is outside a 4-block destination
+    mp = m.ctypes.data_as(ctypes.c_void_p)
+    assert g(FAKE, FAKE, mp, 2, 8, 4, 4096, None) == -8
+    assert g(FAKE, FAKE, mp, 2, 8, 16, 0, None) == -2
+    assert g(FAKE, P(0), mp, 2, 8, 16, 4096, None) == -1
+    m2 = np.array([[-1, 0]], dtype=np.int64)
+    assert g(FAKE, FAKE, m2.ctypes.data_as(ctypes.c_void_p), 1, 8, 16, 4096, None) == -8
