@@ -55,6 +55,18 @@ class Oracle:
         lib.oracle_copy_blocks.restype = ctypes.c_int
         lib.oracle_swap_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I64]
         lib.oracle_swap_blocks.restype = ctypes.c_int
+        lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_to_double.restype = ctypes.c_double
+        lib.oracle_float_to_e4m3.argtypes = [ctypes.c_float]
+        lib.oracle_float_to_e4m3.restype = ctypes.c_uint8
+        lib.oracle_quantize_e4m3.argtypes = [_P, _P, _I64, ctypes.c_float]
+        lib.oracle_quantize_e4m3.restype = None
+        lib.oracle_reshape_and_cache_fp8.argtypes = [_P] * 5 + [_I32] * 5 + [ctypes.c_float] * 2
+        lib.oracle_reshape_and_cache_fp8.restype = ctypes.c_int
+        lib.oracle_decode_fp8_pairs.argtypes = ([_P, _P, _I32, _P, _P, _P, _P, _P] + [_I32] * 6
+                                                + [ctypes.c_double, ctypes.c_float, ctypes.c_float,
+                                                   _P])
+        lib.oracle_decode_fp8_pairs.restype = ctypes.c_int
         self.lib = lib
         self.threads_used = 1
 
@@ -159,6 +171,62 @@ class Oracle:
                                          d_.shape[0], int(np.prod(s_.shape[1:])))
         if rc:
             raise ValueError(f"oracle_swap_blocks failed ({rc})")
+
+    # -- FP8 (OCP E4M3) ------------------------------------------------------------
+    def e4m3_to_double(self, codes):
+        return np.array([self.lib.oracle_e4m3_to_double(int(c)) for c in np.asarray(codes).ravel()],
+                        dtype=np.float64).reshape(np.shape(codes))
+
+    def float_to_e4m3(self, values):
+        v = np.asarray(values, dtype=np.float32)
+        return np.array([self.lib.oracle_float_to_e4m3(float(x)) for x in v.ravel()],
+                        dtype=np.uint8).reshape(v.shape)
+
+    def quantize_e4m3(self, x_f16, scale):
+        x = _u16(np.asarray(x_f16))
+        out = np.empty(x.shape, dtype=np.uint8)
+        self.lib.oracle_quantize_e4m3(_ptr(x), _ptr(out), x.size, float(scale))
+        return out
+
+    def reshape_and_cache_fp8(self, key, value, k_cache8, v_cache8, slot_mapping, k_scale,
+                              v_scale):
+        key, value = _u16(key), _u16(value)
+        assert k_cache8.dtype == np.uint8 and v_cache8.dtype == np.uint8
+        assert k_cache8.flags.c_contiguous and v_cache8.flags.c_contiguous
+        T, H, D = key.shape
+        nb, bs, nh, hd = k_cache8.shape
+        assert (nh, hd) == (H, D)
+        sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        rc = self.lib.oracle_reshape_and_cache_fp8(_ptr(key), _ptr(value), _ptr(k_cache8),
+                                                   _ptr(v_cache8), _ptr(sm), T, H, D, nb, bs,
+                                                   float(k_scale), float(v_scale))
+        if rc:
+            raise ValueError(f"oracle_reshape_and_cache_fp8 failed ({rc})")
+
+    def decode_fp8(self, q, k_cache8, v_cache8, block_tables, context_lens, scale, k_scale,
+                   v_scale, pairs=None):
+        q = _u16(q)
+        S, H, D = q.shape
+        nb, bs, nh, hd = k_cache8.shape
+        assert (nh, hd) == (H, D) and k_cache8.dtype == np.uint8 and v_cache8.shape == k_cache8.shape
+        kc = np.ascontiguousarray(k_cache8)
+        vc = np.ascontiguousarray(v_cache8)
+        whole = pairs is None
+        if whole:
+            pairs = [(s, h) for s in range(S) for h in range(H)]
+        pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        out = np.empty((pr.shape[0], D), dtype=np.float64)
+        used = np.zeros(1, dtype=np.int32)
+        rc = self.lib.oracle_decode_fp8_pairs(_ptr(out), _ptr(pr), pr.shape[0], _ptr(q), _ptr(kc),
+                                              _ptr(vc), _ptr(bt), _ptr(cl), S, H, D, nb, bs,
+                                              bt.shape[1], float(scale), float(k_scale),
+                                              float(v_scale), _ptr(used))
+        if rc:
+            raise ValueError(f"oracle_decode_fp8_pairs failed ({rc})")
+        self.threads_used = int(used[0])
+        return out.reshape(S, H, D) if whole else out
 
 
 _default = None

@@ -15,6 +15,9 @@
  *          §4.2  cache layout in the kernel sketch: K_cache, V_cache are
  *                [num_blocks, block_size, num_heads, head_size]; Q and the
  *                output are [num_heads, head_size] per sequence
+ *          §3.3  FP8 quantisation is listed among the later optimisations; the
+ *                format is not given: we use OCP FP8 E4M3 with one scale per
+ *                cache (see the FP8 section below)
  *   [eng]  "深入解析LLM推理引擎：从PagedAttention到调度优化"
  *          §3.2  block table worked example (block size 4, table [0, 1, 3, ...])
  *          §3.3  the gather is driven by block_table and current_position
@@ -151,6 +154,15 @@ static void attend_contiguous(double *out, const double *q, const double *K, con
     }
 }
 
+/* The query row of (s, h) from q [num_seqs, num_heads, head_dim], decoded. */
+static void load_query(double *qbuf, const uint16_t *q, int32_t s, int32_t h, int32_t num_heads,
+                       int32_t head_dim)
+{
+    const uint16_t *qrow = q + ((int64_t)s * num_heads + h) * head_dim;
+    for (int32_t d = 0; d < head_dim; ++d)
+        qbuf[d] = oracle_half_to_double(qrow[d]);
+}
+
 /* One (sequence, head): gather, then attend.  Scratch buffers are owned by
  * the caller (one set per thread). */
 static int decode_one(double *out, const uint16_t *q,
@@ -165,9 +177,7 @@ static int decode_one(double *out, const uint16_t *q,
                           num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq);
     if (L < 0)
         return L;
-    const uint16_t *qrow = q + ((int64_t)s * num_heads + h) * head_dim;
-    for (int32_t d = 0; d < head_dim; ++d)
-        qbuf[d] = oracle_half_to_double(qrow[d]);
+    load_query(qbuf, q, s, h, num_heads, head_dim);
     attend_contiguous(out, qbuf, Kbuf, Vbuf, L, head_dim, scale, logits);
     return OR_OK;
 }
@@ -350,4 +360,170 @@ int oracle_swap_blocks(const uint16_t *src, uint16_t *dst, const int64_t *mappin
             dst[b * block_elems + e] = src[a * block_elems + e];
     }
     return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * FP8 KV cache ([10x] §3.3 names FP8 quantisation; the format is our reading:
+ * OCP FP8 E4M3, 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 = NaN, largest finite value 448; exponent field 0
+ * holds the subnormals mantissa * 2^-9).  One float scale per cache:
+ * stored code = E4M3(x * (1/scale)) and value = decode(code) * scale.
+ * ------------------------------------------------------------------------- */
+
+double oracle_e4m3_to_double(uint8_t c)
+{
+    int sign = c >> 7;
+    int expo = (c >> 3) & 15;
+    int mant = c & 7;
+    double v;
+    if (expo == 15 && mant == 7)
+        return NAN;
+    if (expo == 0)
+        v = ldexp((double)mant, -9);
+    else
+        v = ldexp((double)(8 + mant), expo - 10); /* (1 + mant/8) * 2^(expo-7) */
+    return sign ? -v : v;
+}
+
+/* Nearest E4M3 code to y, ties to the code with an even mantissa; finite
+ * values beyond the largest code (and +-inf) saturate to +-448; NaN stays NaN.
+ * Written as a search over the 127 non-negative finite codes, whose values
+ * increase with the code. */
+uint8_t oracle_float_to_e4m3(float y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y))
+        return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)y);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    int best = 0;
+    for (int c = 1; c <= 0x7E; ++c) {
+        double dc = fabs(oracle_e4m3_to_double((uint8_t)c) - a);
+        double db = fabs(oracle_e4m3_to_double((uint8_t)best) - a);
+        if (dc < db || (dc == db && (c & 1) == 0))
+            best = c;
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* The scale factor the quantiser multiplies by: 1/scale rounded to float. */
+static float inverse_scale(float scale) { return (float)(1.0 / (double)scale); }
+
+/* codes[i] = E4M3(fp16(x[i]) * (1/scale)), the product rounded to float. */
+void oracle_quantize_e4m3(const uint16_t *x, uint8_t *codes, int64_t n, float scale)
+{
+    float inv = inverse_scale(scale);
+    for (int64_t i = 0; i < n; ++i) {
+        float xf = (float)oracle_half_to_double(x[i]);
+        float y = xf * inv;
+        codes[i] = oracle_float_to_e4m3(y);
+    }
+}
+
+/* reshape_and_cache into FP8 caches: the same slots as the fp16 version,
+ * each value quantised with its cache's scale. */
+int oracle_reshape_and_cache_fp8(const uint16_t *key, const uint16_t *value,
+                                 uint8_t *k_cache, uint8_t *v_cache,
+                                 const int64_t *slot_mapping, int32_t num_tokens,
+                                 int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                                 int32_t block_size, float k_scale, float v_scale)
+{
+    if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
+        return OR_ERR_ARG;
+    int64_t num_slots = (int64_t)num_blocks * block_size;
+    int64_t row = (int64_t)num_heads * head_dim;
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0 || slot >= num_slots)
+            continue;
+        /* [NB, B, H, D]: the rows of slot = block*B + offset start at slot*H*D */
+        oracle_quantize_e4m3(key + t * row, k_cache + slot * row, row, k_scale);
+        oracle_quantize_e4m3(value + t * row, v_cache + slot * row, row, v_scale);
+    }
+    return OR_OK;
+}
+
+/* The paged gather of [10x] §2.3 over FP8 caches, dequantising each value. */
+static int gather_fp8(double *k_out, double *v_out, const uint8_t *k_cache, const uint8_t *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, int32_t seq,
+                      int32_t head, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                      int32_t block_size, int32_t max_blocks_per_seq, float k_scale, float v_scale)
+{
+    int32_t L = context_lens[seq];
+    if (L < 0 || (int64_t)L > (int64_t)max_blocks_per_seq * block_size)
+        return OR_ERR_RANGE;
+    for (int32_t i = 0; i < L; ++i) {
+        int32_t physical = block_tables[(int64_t)seq * max_blocks_per_seq + i / block_size];
+        int32_t offset = i % block_size;
+        if (physical < 0 || physical >= num_blocks)
+            return OR_ERR_RANGE;
+        for (int32_t d = 0; d < head_dim; ++d) {
+            size_t src = cache_index(physical, offset, head, d, block_size, num_heads, head_dim);
+            k_out[(int64_t)i * head_dim + d] = oracle_e4m3_to_double(k_cache[src]) * (double)k_scale;
+            v_out[(int64_t)i * head_dim + d] = oracle_e4m3_to_double(v_cache[src]) * (double)v_scale;
+        }
+    }
+    return L;
+}
+
+/* Decode over FP8 caches for a list of (sequence, head) pairs; the same
+ * conventions as oracle_decode_pairs, q still fp16. */
+int oracle_decode_fp8_pairs(double *out, const int32_t *pairs, int32_t num_pairs,
+                            const uint16_t *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                            int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                            double scale, float k_scale, float v_scale, int32_t *threads_used)
+{
+    int rc = check_shapes(num_seqs, num_heads, head_dim, num_blocks, block_size,
+                          max_blocks_per_seq);
+    if (rc)
+        return rc;
+    int64_t max_len = (int64_t)max_blocks_per_seq * block_size;
+    int status = OR_OK;
+    int nthreads = 1;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        nthreads = omp_get_num_threads();
+#endif
+        double *Kbuf = malloc(sizeof(double) * (size_t)(max_len * head_dim + 1));
+        double *Vbuf = malloc(sizeof(double) * (size_t)(max_len * head_dim + 1));
+        double *qbuf = malloc(sizeof(double) * (size_t)head_dim);
+        double *logits = malloc(sizeof(double) * (size_t)(max_len + 1));
+        int local = (Kbuf && Vbuf && qbuf && logits) ? OR_OK : OR_ERR_NOMEM;
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t p = 0; p < num_pairs; ++p) {
+            if (local)
+                continue;
+            int32_t s = pairs[2 * p], h = pairs[2 * p + 1];
+            if (s < 0 || s >= num_seqs || h < 0 || h >= num_heads) {
+                local = OR_ERR_ARG;
+                continue;
+            }
+            int L = gather_fp8(Kbuf, Vbuf, k_cache, v_cache, block_tables, context_lens, s, h,
+                               num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
+                               k_scale, v_scale);
+            if (L < 0) {
+                local = L;
+                continue;
+            }
+            load_query(qbuf, q, s, h, num_heads, head_dim);
+            attend_contiguous(out + (int64_t)p * head_dim, qbuf, Kbuf, Vbuf, L, head_dim, scale,
+                              logits);
+        }
+        if (local) {
+#pragma omp critical
+            status = local;
+        }
+        free(Kbuf);
+        free(Vbuf);
+        free(qbuf);
+        free(logits);
+    }
+    if (threads_used)
+        *threads_used = nthreads;
+    return status;
 }

@@ -22,6 +22,12 @@ What pins what:
   copy / swap      numpy block assignment on random bit patterns; a
                    copy-on-write sequence ("vLLM基础架构" §2.3) seen through
                    the gather; out-of-range pairs
+  FP8 (OCP E4M3)   all 256 codes vs torch.float8_e4m3fn; the encoder vs
+                   torch's float -> float8_e4m3fn cast wherever torch does not
+                   overflow (all fp16 values, ties, random floats), closed forms
+                   for saturation and NaN; the scaled quantiser vs torch doing
+                   the float32 multiply and cast; FP8 decode vs torch SDPA on
+                   the dequantised contiguous K/V
 """
 import json
 import math
@@ -371,10 +377,111 @@ def pin_swap_blocks(orc):
         raise AssertionError("out-of-range swap accepted")
 
 
+def _torch_e4m3_codes(y_f32):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(y_f32, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_decode_exhaustive(orc):
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.e4m3_to_double(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # the format's landmarks
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+    assert got[0x7E] == 448.0 and np.isnan(got[0x7F]) and got[0xFE] == -448.0
+
+
+def pin_e4m3_encode(orc):
+    rng = np.random.default_rng(10)
+    f16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    ys = [f16.astype(np.float32)[np.isfinite(f16)]]
+    # exact midpoints between neighbouring codes (ties) and their neighbours
+    vals = orc.e4m3_to_double(np.arange(0x7F, dtype=np.uint8))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    ys += [mids, -mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))]
+    ys += [rng.standard_normal(20000).astype(np.float32) * np.float32(50.0),
+           (rng.random(20000) * 2.0 ** -8).astype(np.float32)]
+    y = np.concatenate(ys).astype(np.float32)
+    got = orc.float_to_e4m3(y)
+    small = np.abs(y) < 464.0   # torch's cast is defined (no NaN) only below 464
+    assert np.array_equal(got[small], _torch_e4m3_codes(y[small]))
+    big = ~small
+    assert np.all(got[big] == np.where(np.signbit(y[big]), 0xFE, 0x7E))
+    special = np.array([np.inf, -np.inf, np.nan, -np.nan, 1e30, -1e-30, 0.0, -0.0], np.float32)
+    assert orc.float_to_e4m3(special).tolist() == [0x7E, 0xFE, 0x7F, 0xFF, 0x7E, 0x80, 0x00, 0x80]
+
+
+def pin_quantize_scale(orc):
+    import torch
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(50000) * 3).astype(np.float16)
+    for scale in (1.0, 0.02, 1 / 64.0, 3.7):
+        got = orc.quantize_e4m3(x, scale)
+        inv = torch.tensor(1.0 / scale, dtype=torch.float64).float()
+        y = (torch.from_numpy(x.astype(np.float32)) * inv).numpy()
+        ref = np.where(np.abs(y) >= 464.0, np.where(np.signbit(y), 0xFE, 0x7E),
+                       _torch_e4m3_codes(np.clip(y, -463.0, 463.0))).astype(np.uint8)
+        assert np.array_equal(got, ref), scale
+
+
+def pin_fp8_decode_sdpa(orc):
+    import torch
+    rng = np.random.default_rng(12)
+    S, H, D, B = 3, 2, 128, 16
+    lens = np.array([1, 37, 80])
+    MB = 5
+    bt = (np.arange(S)[:, None] * MB + np.arange(MB)[None, :]).astype(np.int32)
+    NB = S * MB
+    q = _f16(rng.standard_normal((S, H, D)))
+    kc = rng.integers(0, 256, size=(NB, B, H, D), dtype=np.uint32).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(NB, B, H, D), dtype=np.uint32).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x3C   # no NaN codes in live data
+    vc[(vc & 0x7F) == 0x7F] = 0x3C
+    ks, vs = 0.01, 0.05
+    got = orc.decode_fp8(q, kc, vc, bt, lens.astype(np.int32), 0.0884, ks, vs)
+    Kd = torch.from_numpy(kc).view(torch.float8_e4m3fn).double() * float(np.float32(ks))
+    Vd = torch.from_numpy(vc).view(torch.float8_e4m3fn).double() * float(np.float32(vs))
+    for s in range(S):
+        L = int(lens[s])
+        Kc = Kd[s * MB:(s + 1) * MB].reshape(MB * B, H, D)[:L]
+        Vc = Vd[s * MB:(s + 1) * MB].reshape(MB * B, H, D)[:L]
+        for h in range(H):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[s, h].astype(np.float64)).reshape(1, 1, D),
+                Kc[:, h].reshape(1, L, D).contiguous(), Vc[:, h].reshape(1, L, D).contiguous(),
+                scale=0.0884).reshape(D).numpy()
+            assert np.allclose(got[s, h], ref, rtol=1e-11, atol=1e-13), (s, h)
+
+
+def pin_fp8_reshape(orc):
+    rng = np.random.default_rng(13)
+    NB, B, H, D, T = 6, 16, 2, 64, 5
+    kc = np.full((NB, B, H, D), 0xA5, dtype=np.uint8)
+    vc = np.full((NB, B, H, D), 0x5A, dtype=np.uint8)
+    key = _f16(rng.standard_normal((T, H, D)) * 4)
+    val = _f16(rng.standard_normal((T, H, D)) * 4)
+    slots = rng.choice(NB * B, size=T, replace=False).astype(np.int64)
+    slots[0] = -1          # padding token
+    slots[1] = NB * B      # one past the pool
+    orc.reshape_and_cache_fp8(key, val, kc, vc, slots, 0.05, 0.02)
+    rk = np.full((NB * B, H, D), 0xA5, dtype=np.uint8)
+    rv = np.full((NB * B, H, D), 0x5A, dtype=np.uint8)
+    rk[slots[2:]] = orc.quantize_e4m3(key[2:], 0.05)
+    rv[slots[2:]] = orc.quantize_e4m3(val[2:], 0.02)
+    assert np.array_equal(kc.reshape(NB * B, H, D), rk) and np.array_equal(vc.reshape(NB * B, H, D), rv)
+
+
 PINS = [pin_half_decode_exhaustive, pin_gather_worked_example, pin_contiguous_sdpa,
         pin_block_permutation_invariance, pin_brute_force_tiny, pin_closed_forms, pin_needles,
         pin_reshape_scatter, pin_reshape_worked_example, pin_copy_blocks, pin_copy_on_write,
-        pin_swap_blocks]
+        pin_swap_blocks, pin_e4m3_decode_exhaustive, pin_e4m3_encode, pin_quantize_scale,
+        pin_fp8_decode_sdpa, pin_fp8_reshape]
 
 
 def main(argv):
@@ -388,6 +495,8 @@ def main(argv):
             pin(orc)
         except Exception as e:  # noqa: BLE001 - any failure is a caught mistake
             failed.append(f"{pin.__name__}: {type(e).__name__}: {str(e)[:120]}")
+            if "--fail-fast" in argv:
+                break
     for f in failed:
         print("FAIL", f)
     print(f"{len(PINS) - len(failed)}/{len(PINS)} pins passed")

@@ -18,7 +18,11 @@ SRC = os.path.join(ROOT, "oracle", "pa_oracle.c")
 MUTANTS = {
     "block_index_mod": ("int32_t logical_block = i / block_size;",
                         "int32_t logical_block = i % block_size;"),
-    "offset_div": ("int32_t offset = i % block_size;", "int32_t offset = i / block_size;"),
+    "offset_div": ("int32_t logical_block = i / block_size;\n        int32_t offset = i % block_size;",
+                   "int32_t logical_block = i / block_size;\n        int32_t offset = i / block_size;"),
+    "fp8_gather_offset_div": ("int32_t offset = i % block_size;\n        if (physical < 0",
+                              "int32_t offset = i / block_size;\n        if (physical < 0"),
+    "fp8_gather_block_mod": ("max_blocks_per_seq + i / block_size];", "max_blocks_per_seq + i % block_size];"),
     "drop_last_token": ("for (int32_t i = 0; i < L; ++i) {\n        int32_t logical_block",
                         "for (int32_t i = 0; i < L - 1; ++i) {\n        int32_t logical_block"),
     "drop_first_token": ("for (int32_t i = 0; i < L; ++i) {\n        double w",
@@ -42,7 +46,10 @@ MUTANTS = {
                              "v = ldexp((double)frac, expo - 25);"),
     "half_nan_as_inf": ("v = frac ? NAN : INFINITY;", "v = INFINITY;"),
     "reshape_block_mod": ("int64_t block = slot / block_size;", "int64_t block = slot % block_size;"),
-    "reshape_no_upper_check": ("if (slot < 0 || slot >= num_slots)", "if (slot < 0)"),
+    "reshape_no_upper_check": ("if (slot < 0 || slot >= num_slots)\n            continue;\n        int64_t block",
+                               "if (slot < 0)\n            continue;\n        int64_t block"),
+    "fp8_reshape_no_upper_check": ("if (slot < 0 || slot >= num_slots)\n            continue;\n        /*",
+                                   "if (slot < 0)\n            continue;\n        /*"),
     "reshape_value_gets_key": ("v_cache[dst] = value[src];", "v_cache[dst] = key[src];"),
     "copy_direction": ("k_cache[dst * block_elems + e] = k_cache[src * block_elems + e];",
                        "k_cache[src * block_elems + e] = k_cache[dst * block_elems + e];"),
@@ -50,6 +57,19 @@ MUTANTS = {
     "swap_no_range_check": ("        if (a < 0 || a >= src_blocks || b < 0 || b >= dst_blocks)\n            return OR_ERR_RANGE;\n", ""),
     "swap_uses_dst_index_for_src": ("dst[b * block_elems + e] = src[a * block_elems + e];",
                                     "dst[b * block_elems + e] = src[b * block_elems + e];"),
+    "e4m3_bias": ("v = ldexp((double)(8 + mant), expo - 10);", "v = ldexp((double)(8 + mant), expo - 9);"),
+    "e4m3_subnormal": ("v = ldexp((double)mant, -9);", "v = ldexp((double)mant, -10);"),
+    "e4m3_no_nan": ("    if (expo == 15 && mant == 7)\n        return NAN;\n", ""),
+    "e4m3_ties_away": ("if (dc < db || (dc == db && (c & 1) == 0))", "if (dc < db || dc == db)"),
+    "e4m3_ties_down": ("if (dc < db || (dc == db && (c & 1) == 0))", "if (dc < db)"),
+    "e4m3_overflow_to_nan": ("        return (uint8_t)(sign | 0x7E);", "        return (uint8_t)(sign | 0x7F);"),
+    "fp8_k_scale_dropped": ("oracle_e4m3_to_double(k_cache[src]) * (double)k_scale;",
+                            "oracle_e4m3_to_double(k_cache[src]);"),
+    "fp8_v_from_k": ("oracle_e4m3_to_double(v_cache[src]) * (double)v_scale;",
+                     "oracle_e4m3_to_double(k_cache[src]) * (double)v_scale;"),
+    "fp8_reshape_value_k_scale": ("oracle_quantize_e4m3(value + t * row, v_cache + slot * row, row, v_scale);",
+                                  "oracle_quantize_e4m3(value + t * row, v_cache + slot * row, row, k_scale);"),
+    "fp8_quantize_scale_not_inverted": ("float y = xf * inv;", "float y = xf * scale;"),
 }
 
 
@@ -63,7 +83,8 @@ def test_mutant_is_caught(name, tmp_path):
     src = tmp_path / f"{name}.c"
     src.write_text(text.replace(old, new))
     lib = obuild.build(str(src), str(tmp_path / f"lib{name}.so"), quiet=True)
-    r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), "--lib", lib],
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), "--lib", lib,
+                        "--fail-fast"],
                        capture_output=True, text=True, timeout=300,
                        env={**os.environ, "OMP_NUM_THREADS": "2"})
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
