@@ -6,7 +6,8 @@
  *   [10x]  "vLLM推理加速深度解读：PagedAttention如何提升10x吞吐量"
  *          §2.1 attention equation; §2.3 paged attention equations and the
  *          gather K_paged[i] = K_physical[BlockTable[i / B]][i mod B];
- *          §4.2 cache layout [num_blocks, block_size, num_heads, head_size]
+ *          §4.2 cache layout [num_blocks, block_size, num_heads, head_size];
+ *          §3.3 FP8 quantisation (named only)
  *   [eng]  "深入解析LLM推理引擎：从PagedAttention到调度优化"
  *          §3.2 on-demand block filling and the block table; §3.3 the gather
  *          driven by block_table and the current position
@@ -133,6 +134,41 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
               int32_t max_blocks_per_seq, float scale, int32_t partition_size,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * FP8 KV cache.  [10x] §3.3 names FP8 quantisation without fixing a format;
+ * the reading used here is OCP FP8 E4M3 (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits, no infinities, S.1111.111 = NaN, largest value 448)
+ * with one float scale per cache: code = E4M3(x * (1/scale)) where the
+ * product is rounded to float and then to the nearest E4M3 value (ties to
+ * even); finite values beyond +-448 saturate to +-448 and NaN stays NaN.  A
+ * code decodes to value(code) * scale.  Caches hold one byte per element in
+ * the same [num_blocks, block_size, num_heads, head_dim] layout.
+ */
+
+/*
+ * pa_reshape_and_cache for FP8 caches: the same slots and skip rule as
+ * pa_reshape_and_cache; each fp16 value of key (value) is quantised with
+ * k_scale (v_scale).  Scales must be finite and > 0; head_dim % 16 == 0.
+ * The codes are bit-exact for the rule above.
+ */
+int pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                             float k_scale, float v_scale, void* stream);
+
+/*
+ * pa_decode over FP8 caches: the same arguments, semantics, workspace
+ * (pa_decode_workspace_size) and errors as pa_decode, with k_cache / v_cache
+ * holding E4M3 codes and K_paged, V_paged replaced by value(code) * k_scale
+ * and value(code) * v_scale.  q and out stay fp16; the arithmetic is fp32
+ * (codes are widened exactly).  Scales must be finite and > 0.
+ */
+int pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                  int32_t max_blocks_per_seq, float scale, float k_scale, float v_scale,
+                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Copy whole physical blocks inside one cache pair: the copy-on-write step

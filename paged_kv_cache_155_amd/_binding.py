@@ -44,6 +44,12 @@ def load(path=None):
     lib.pa_decode.argtypes = ([_P] * 6 + [_I32] * 6 + [ctypes.c_float, _I32, _P, ctypes.c_size_t,
                                                        _P])
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_reshape_and_cache_fp8.argtypes = ([_P, _P, _P, _P, _P] + [_I32] * 5
+                                             + [ctypes.c_float, ctypes.c_float, _P])
+    lib.pa_reshape_and_cache_fp8.restype = ctypes.c_int
+    lib.pa_decode_fp8.argtypes = ([_P] * 6 + [_I32] * 6 + [ctypes.c_float] * 3
+                                  + [_I32, _P, ctypes.c_size_t, _P])
+    lib.pa_decode_fp8.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_swap_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, ctypes.c_int64, _P]
@@ -185,3 +191,61 @@ def swap_blocks(src, dst, block_mapping, stream=None):
                                dst.shape[0], block_bytes, _stream_ptr(stream))
     if rc != PA_OK:
         raise PAError(rc, "pa_swap_blocks")
+
+
+def _check_fp8_cache(t, name, shape=None):
+    import torch
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    _check(t, name, t.dtype, shape=shape, ndim=4)
+
+
+def reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale,
+                          stream=None):
+    """reshape_and_cache into FP8 (OCP E4M3) caches [NB, B, H, D] of uint8 /
+    float8_e4m3fn, quantising with code = E4M3(x * (1/scale))."""
+    import torch
+    _check_fp8_cache(k_cache, "k_cache")
+    NB, B, H, D = k_cache.shape
+    _check_fp8_cache(v_cache, "v_cache", shape=k_cache.shape)
+    _check(key, "key", torch.float16, ndim=3)
+    T = key.shape[0]
+    _check(key, "key", torch.float16, shape=(T, H, D))
+    _check(value, "value", torch.float16, shape=(T, H, D))
+    _check(slot_mapping, "slot_mapping", torch.int64, shape=(T,))
+    rc = load().pa_reshape_and_cache_fp8(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(slot_mapping), T, H, D, NB, B, float(k_scale),
+                                         float(v_scale), _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_reshape_and_cache_fp8")
+
+
+def decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+               partition_size=512, workspace=None, stream=None):
+    """Paged-attention decode over FP8 caches (values = code * scale); the
+    other arguments as decode()."""
+    import torch
+    _check_fp8_cache(k_cache, "k_cache")
+    NB, B, H, D = k_cache.shape
+    _check_fp8_cache(v_cache, "v_cache", shape=k_cache.shape)
+    _check(q, "q", torch.float16, ndim=3)
+    S = q.shape[0]
+    _check(q, "q", torch.float16, shape=(S, H, D))
+    _check(out, "out", torch.float16, shape=(S, H, D))
+    _check(block_tables, "block_tables", torch.int32, ndim=2)
+    MB = block_tables.shape[1]
+    _check(block_tables, "block_tables", torch.int32, shape=(S, MB))
+    _check(context_lens, "context_lens", torch.int32, shape=(S,))
+    need = decode_workspace_size(S, H, D, B, MB, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if need else None
+    elif need:
+        _check(workspace, "workspace", torch.uint8, ndim=1)
+    wbytes = workspace.numel() if workspace is not None else 0
+    rc = load().pa_decode_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(block_tables), _ptr(context_lens), S, H, D, NB, B, MB,
+                              float(scale), float(k_scale), float(v_scale), int(partition_size),
+                              _ptr(workspace), wbytes, _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_decode_fp8")
+    return out

@@ -104,11 +104,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
     return layout((int64_t)num_seqs * num_heads * np, head_dim).total;
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-              int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
-              int32_t max_blocks_per_seq, float scale, int32_t partition_size, void* workspace,
-              size_t workspace_bytes, void* stream)
+namespace {
+
+// Shared checks and parameter set-up of pa_decode and pa_decode_fp8.
+int prepare_decode(pa::DecodeParams& p, void* out, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                   int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                   int32_t block_size, int32_t max_blocks_per_seq, float scale,
+                   int32_t partition_size, void* workspace, size_t workspace_bytes)
 {
     if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0 ||
         max_blocks_per_seq <= 0)
@@ -122,7 +125,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     if (!std::isfinite(scale))
         return PA_ERR_INVALID_DIM;
     if (num_seqs == 0)
-        return PA_OK;
+        return 1;  // nothing to enqueue
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
         return PA_ERR_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
@@ -135,11 +138,11 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     if (units > INT32_MAX || (int64_t)num_seqs * num_heads > INT32_MAX)
         return PA_ERR_INVALID_DIM;
 
-    pa::DecodeParams p{};
+    p = pa::DecodeParams{};
     p.out = static_cast<_Float16*>(out);
     p.q = static_cast<const _Float16*>(q);
-    p.k_cache = static_cast<const _Float16*>(k_cache);
-    p.v_cache = static_cast<const _Float16*>(v_cache);
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.num_seqs = num_seqs;
@@ -149,6 +152,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     p.num_partitions = (int32_t)np;
     p.total_units = (uint32_t)units;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
+    p.v_scale = 1.0f;
     if (np > 1) {
         const WorkspaceLayout w = layout(units, head_dim);
         if (!workspace || workspace_bytes < w.total)
@@ -160,8 +164,79 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
         p.ws_m = reinterpret_cast<float*>(base + w.o_bytes);
         p.ws_l = reinterpret_cast<float*>(base + w.o_bytes + w.m_bytes);
     }
+    return PA_OK;
+}
+
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+
+}  // namespace
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+              int32_t max_blocks_per_seq, float scale, int32_t partition_size, void* workspace,
+              size_t workspace_bytes, void* stream)
+{
+    pa::DecodeParams p;
+    int rc = prepare_decode(p, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                            num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq, scale,
+                            partition_size, workspace, workspace_bytes);
+    if (rc != PA_OK)
+        return rc == 1 ? PA_OK : rc;
     hipError_t e = pa::launch_decode_dispatch(p, head_dim, block_size,
                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                  int32_t max_blocks_per_seq, float scale, float k_scale, float v_scale,
+                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!valid_scale(k_scale) || !valid_scale(v_scale))
+        return PA_ERR_INVALID_DIM;
+    pa::DecodeParams p;
+    int rc = prepare_decode(p, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                            num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq, scale,
+                            partition_size, workspace, workspace_bytes);
+    if (rc != PA_OK)
+        return rc == 1 ? PA_OK : rc;
+    p.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634074);
+    p.v_scale = v_scale;
+    hipError_t e = pa::launch_decode_fp8_dispatch(p, head_dim, block_size,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, int32_t num_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                             float k_scale, float v_scale, void* stream)
+{
+    if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
+        return PA_ERR_INVALID_DIM;
+    if (!valid_scale(k_scale) || !valid_scale(v_scale))
+        return PA_ERR_INVALID_DIM;
+    if (head_dim % 16 != 0)
+        return PA_ERR_UNSUPPORTED;
+    if ((int64_t)num_heads * head_dim > INT32_MAX)
+        return PA_ERR_INVALID_DIM;
+    if (num_tokens == 0)
+        return PA_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+        return PA_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+        return PA_ERR_ALIGN;
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    // the quantiser multiplies by 1/scale rounded to float
+    const float k_inv = (float)(1.0 / (double)k_scale);
+    const float v_inv = (float)(1.0 / (double)v_scale);
+    hipError_t e = pa::launch_reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping,
+                                                    num_tokens, num_slots, num_heads * head_dim,
+                                                    k_inv, v_inv,
+                                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

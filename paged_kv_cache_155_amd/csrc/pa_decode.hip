@@ -1,4 +1,5 @@
-// Paged-attention decode kernels for gfx950 (MI355X), fp16 KV, fp32 math.
+// Paged-attention decode kernels for gfx950 (MI355X): fp16 or FP8 (OCP E4M3)
+// KV cache, fp16 queries, fp32 math.
 //
 // Sources (web pages), cited by title and section:
 //   [10x]  "vLLM推理加速深度解读：PagedAttention如何提升10x吞吐量"
@@ -6,7 +7,9 @@
 //          K_paged[i] = K_physical[BlockTable[i / B]][i mod B];
 //          §4.2 kernel strategy (walk the context block by block, keep the
 //          block table close, one group of lanes per query head) and the
-//          cache layout [num_blocks, block_size, num_heads, head_size]
+//          cache layout [num_blocks, block_size, num_heads, head_size];
+//          §3.3 FP8 quantisation (format not given; OCP E4M3 with one scale
+//          per cache is our reading)
 //   [eng]  "深入解析LLM推理引擎：从PagedAttention到调度优化" §3.3 (the
 //          gather follows block_table up to the current position)
 //
@@ -21,20 +24,22 @@
 //     a ragged batch are spread evenly over time;
 //   * K/V are streamed with nontemporal loads (read once, so they should not
 //     displace other lines in the caches);
-//   * a wave walks 32-token tiles (64 for head_dim 64).  For head_dim 128 a
-//     token's row of one head is 256 contiguous bytes = 16 lanes x 16 bytes,
-//     so one global_load_dwordx4 covers 4 tokens; a tile issues 8 K loads
-//     and 8 V loads per lane before any arithmetic;
+//   * every lane loads 16 bytes of a token's row of one head (8 fp16 or 16
+//     FP8 values).  For fp16 and head_dim 128 that is 16 lanes per token and
+//     4 tokens per global_load_dwordx4; FP8 halves the lanes per token.  A
+//     wave walks tiles of 8 loads (32 tokens for fp16 / 128, 64 for FP8 /
+//     128) and issues all 8 K and 8 V loads before any arithmetic;
 //   * block ids: each wave reads up to 64 table entries with one vector load
 //     and pulls the one a load needs with v_readlane (a scalar), so the
 //     K/V address of a whole load is scalar base + lane offset;
-//   * q.k with v_dot2_f32_f16 (fp16 products, fp32 sum), then a 16-lane
-//     DPP butterfly (quad_perm, row_half_mirror, row_mirror) - no LDS;
+//   * q.k with v_dot2_f32_f16 (fp16 products, fp32 sum; FP8 codes are first
+//     widened exactly to fp16 pairs), then a DPP butterfly over the lanes of
+//     a token (quad_perm, row_half_mirror, row_mirror) - no LDS;
 //   * online softmax per lane group (running max m, sum l, fp32 row
 //     accumulator, rescaled once per tile), merged across lane groups with
-//     shuffles and across waves through 2 KB of LDS, in fixed order;
-//   * base-2 exponent: logits are scaled by scale*log2(e) and exponentiated
-//     with v_exp_f32;
+//     shuffles and across waves through LDS, in a fixed order;
+//   * base-2 exponent: logits are scaled by scale*log2(e) (times the K scale
+//     for FP8) and exponentiated with v_exp_f32;
 //   * split context: each partition writes (m, l, normalised row) to the
 //     workspace; pa_reduce merges them with the log-sum-exp identity.
 //     A single-partition (sequence, head) writes its fp16 row directly.
@@ -54,6 +59,7 @@ constexpr int kLoads = 8;  // K (and V) 16-byte loads per lane per tile
 constexpr float kNegInf = -__builtin_inff();
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
@@ -65,15 +71,17 @@ __device__ __forceinline__ float dpp_mov(float v)
         0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of kLanes lanes (8 or 16); every lane of a group
-// ends with the group sum.  quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// Sum over aligned groups of kLanes lanes (4, 8 or 16); every lane of a
+// group ends with the group sum.  quad_perm [1,0,3,2], quad_perm [2,3,0,1],
 // row_half_mirror, row_mirror.
 template <int kLanes>
 __device__ __forceinline__ float group_sum(float v)
 {
+    static_assert(kLanes == 4 || kLanes == 8 || kLanes == 16, "group of 4, 8 or 16 lanes");
     v += dpp_mov<0xB1>(v);
     v += dpp_mov<0x4E>(v);
-    v += dpp_mov<0x141>(v);
+    if constexpr (kLanes >= 8)
+        v += dpp_mov<0x141>(v);
     if constexpr (kLanes == 16)
         v += dpp_mov<0x140>(v);
     return v;
@@ -86,11 +94,6 @@ __device__ __forceinline__ int readlane(int v, int lane)
     return __builtin_amdgcn_readlane(v, lane);
 }
 
-__device__ __forceinline__ float readlane_f(float v, int lane)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
-}
-
 // Hardware workgroup i of n lands on XCD i % 8.  Give XCD x the contiguous
 // logical range [x*n/8, (x+1)*n/8) (remainder spread over the first XCDs).
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n)
@@ -101,48 +104,93 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n)
     return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
 
-struct LaneState {
-    float m;       // running maximum of base-2 logits (group-uniform)
-    float l;       // running sum of exp2(logit - m)
-    float acc[8];  // running sum of exp2(logit - m) * v over this lane's 8 columns
+// ---- cache element types -------------------------------------------------
+// Each lane holds 16 bytes of one token's row: kElems values, whose q
+// counterparts are kElems/2 fp16 pairs.  dot() is the lane's share of q.k;
+// the V update is written out in tile_step (as a called helper the compiler
+// stops keeping the accumulators in registers).
+
+struct KvF16 {
+    static constexpr int kElemBytes = 2;
+    static constexpr int kElems = 8;
+    static constexpr bool kScaledOutput = false;
+    // partial q.k over this lane's 8 values
+    __device__ static __forceinline__ float dot(const u32x4& k, const h2* q)
+    {
+        float d = __builtin_amdgcn_fdot2(as_h2(k.x), q[0], 0.0f, false);
+        d = __builtin_amdgcn_fdot2(as_h2(k.y), q[1], d, false);
+        d = __builtin_amdgcn_fdot2(as_h2(k.z), q[2], d, false);
+        return __builtin_amdgcn_fdot2(as_h2(k.w), q[3], d, false);
+    }
 };
 
-template <int D, int B>
+struct KvFp8 {
+    static constexpr int kElemBytes = 1;
+    static constexpr int kElems = 16;
+    static constexpr bool kScaledOutput = true;
+    // Widen byte pair kHi (low or high half of w) to an exact fp16 pair.
+    template <bool kHi>
+    __device__ static __forceinline__ h2 widen(uint32_t w)
+    {
+        return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi);
+    }
+    __device__ static __forceinline__ float dot(const u32x4& k, const h2* q)
+    {
+        const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+        float d = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d = __builtin_amdgcn_fdot2(widen<false>(w[i]), q[2 * i], d, false);
+            d = __builtin_amdgcn_fdot2(widen<true>(w[i]), q[2 * i + 1], d, false);
+        }
+        return d;
+    }
+};
+
+template <typename KV>
+struct LaneState {
+    float m;                // running maximum of base-2 logits (group-uniform)
+    float l;                // running sum of exp2(logit - m)
+    float acc[KV::kElems];  // running sum of exp2(logit - m) * v over this lane's columns
+};
+
+template <typename KV, int D, int B>
 struct Geometry {
-    static constexpr int kLanesPerToken = D / 8;              // 16 B per lane
+    static constexpr int kLanesPerToken = D / KV::kElems;    // 16 bytes per lane
     static constexpr int kTokensPerLoad = kWave / kLanesPerToken;
     static constexpr int kTile = kLoads * kTokensPerLoad;     // tokens per wave step
     static_assert(kTile % B == 0 || B % kTile == 0, "tile / block mismatch");
     static_assert(B % kTokensPerLoad == 0, "a load must stay in one block");
 };
 
+template <typename KV>
 struct TileCtx {
-    const _Float16* k;
-    const _Float16* v;
-    int64_t block_elems;  // B * H * D
-    int lane_elem;        // (g * H + h) * D + lt * 8, for in-block offset 0
-    int token_stride;     // H * D elements between consecutive in-block offsets
+    const char* k;
+    const char* v;
+    int64_t block_bytes;  // B * H * D * element bytes
+    int lane_byte;        // ((g * H + h) * D + lt * kElems) * element bytes, in-block offset 0
+    int token_stride;     // H * D * element bytes between consecutive in-block offsets
     int group;            // lane / lanes-per-token
     int end;              // first logical position not attended by this partition
     float scale_log2;
-    h2 q[4];
+    h2 q[KV::kElems / 2];
 };
 
 // One tile of kTile tokens starting at logical position t0 (a multiple of
 // the tile).  ids holds table entries [chunk0, chunk0 + 64) in lane order.
-template <int D, int B, bool kMasked>
-__device__ __forceinline__ void tile_step(LaneState& st, const TileCtx& c, int t0, int ids,
-                                          int chunk0)
+template <typename KV, int D, int B, bool kMasked>
+__device__ __forceinline__ void tile_step(LaneState<KV>& st, const TileCtx<KV>& c, int t0,
+                                          int ids, int chunk0)
 {
-    using G = Geometry<D, B>;
+    using G = Geometry<KV, D, B>;
     u32x4 kr[kLoads], vr[kLoads];
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
         const int tj = t0 + j * G::kTokensPerLoad;  // first token of this load (uniform)
         if (!kMasked || tj < c.end) {
             const int pb = readlane(ids, tj / B - chunk0);
-            const int64_t e = (int64_t)pb * c.block_elems + (int64_t)((tj % B) * c.token_stride) +
-                              c.lane_elem;
+            const int64_t e = (int64_t)pb * c.block_bytes + (int64_t)((tj % B) * c.token_stride) +
+                              c.lane_byte;
             kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c.k + e));
             vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c.v + e));
         } else {
@@ -154,11 +202,7 @@ __device__ __forceinline__ void tile_step(LaneState& st, const TileCtx& c, int t
     float tmax = kNegInf;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
-        float d = __builtin_amdgcn_fdot2(as_h2(kr[j].x), c.q[0], 0.0f, false);
-        d = __builtin_amdgcn_fdot2(as_h2(kr[j].y), c.q[1], d, false);
-        d = __builtin_amdgcn_fdot2(as_h2(kr[j].z), c.q[2], d, false);
-        d = __builtin_amdgcn_fdot2(as_h2(kr[j].w), c.q[3], d, false);
-        d = group_sum<G::kLanesPerToken>(d) * c.scale_log2;
+        float d = group_sum<G::kLanesPerToken>(KV::dot(kr[j], c.q)) * c.scale_log2;
         if (kMasked) {
             const bool valid = t0 + j * G::kTokensPerLoad + c.group < c.end;
             d = valid ? d : kNegInf;
@@ -172,42 +216,58 @@ __device__ __forceinline__ void tile_step(LaneState& st, const TileCtx& c, int t
     const float alpha = exp2_fast(st.m - m_ref);
     st.l *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < KV::kElems; ++i)
         st.acc[i] *= alpha;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
         const float p = exp2_fast(x[j] - m_ref);
         st.l += p;
         const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+        if constexpr (KV::kElemBytes == 2) {  // acc += p * v, 8 fp16 values
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const h2 v2 = as_h2(w[i]);
-            st.acc[2 * i] = fmaf(p, (float)v2.x, st.acc[2 * i]);
-            st.acc[2 * i + 1] = fmaf(p, (float)v2.y, st.acc[2 * i + 1]);
+            for (int i = 0; i < 4; ++i) {
+                const h2 v2 = as_h2(w[i]);
+                st.acc[2 * i] = fmaf(p, (float)v2.x, st.acc[2 * i]);
+                st.acc[2 * i + 1] = fmaf(p, (float)v2.y, st.acc[2 * i + 1]);
+            }
+        } else {  // acc += p * v, 16 FP8 codes decoded exactly to fp32
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+                const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+                st.acc[4 * i] = fmaf(p, lo.x, st.acc[4 * i]);
+                st.acc[4 * i + 1] = fmaf(p, lo.y, st.acc[4 * i + 1]);
+                st.acc[4 * i + 2] = fmaf(p, hi.x, st.acc[4 * i + 2]);
+                st.acc[4 * i + 3] = fmaf(p, hi.y, st.acc[4 * i + 3]);
+            }
         }
     }
     st.m = m_new;
 }
 
 // Merge (m, l, acc) of two partial softmax states with the log-sum-exp rule.
-__device__ __forceinline__ void merge_into(LaneState& st, float m_o, float l_o, const float* acc_o)
+template <typename KV>
+__device__ __forceinline__ void merge_into(LaneState<KV>& st, float m_o, float l_o,
+                                           const float* acc_o)
 {
     const float M = fmaxf(st.m, m_o);
     const float Mr = M == kNegInf ? 0.0f : M;
     const float wa = exp2_fast(st.m - Mr), wb = exp2_fast(m_o - Mr);
     st.l = st.l * wa + l_o * wb;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < KV::kElems; ++i)
         st.acc[i] = st.acc[i] * wa + acc_o[i] * wb;
     st.m = M;
 }
 
-template <int D, int B>
+template <typename KV, int D, int B>
 __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
 {
-    using G = Geometry<D, B>;
+    using G = Geometry<KV, D, B>;
     constexpr int LPT = G::kLanesPerToken;
     constexpr int TILE = G::kTile;
+    constexpr int E = KV::kElems;
+    constexpr int EB = KV::kElemBytes;
 
     const uint32_t logical = xcd_remap(blockIdx.x, P.total_units);
     const int s = (int)(logical % (uint32_t)P.num_seqs);
@@ -231,28 +291,29 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
     const int end = min(p0 + P.partition_size, ctx);
     const int nparts_seq = (ctx + P.partition_size - 1) / P.partition_size;
 
-    TileCtx c;
-    c.k = P.k_cache;
-    c.v = P.v_cache;
-    c.block_elems = (int64_t)B * P.num_heads * D;
+    TileCtx<KV> c;
+    c.k = static_cast<const char*>(P.k_cache);
+    c.v = static_cast<const char*>(P.v_cache);
+    c.block_bytes = (int64_t)B * P.num_heads * D * EB;
     c.group = lane / LPT;
-    c.token_stride = P.num_heads * D;
-    c.lane_elem = (c.group * P.num_heads + h) * D + (lane % LPT) * 8;
+    c.token_stride = P.num_heads * D * EB;
+    c.lane_byte = ((c.group * P.num_heads + h) * D + (lane % LPT) * E) * EB;
     c.end = end;
     c.scale_log2 = P.scale_log2;
-    {
-        const u32x4 qv = *reinterpret_cast<const u32x4*>(P.q + row + (lane % LPT) * 8);
-        c.q[0] = as_h2(qv.x);
-        c.q[1] = as_h2(qv.y);
-        c.q[2] = as_h2(qv.z);
-        c.q[3] = as_h2(qv.w);
+#pragma unroll
+    for (int i = 0; i < E / 8; ++i) {
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(P.q + row + (lane % LPT) * E + 8 * i);
+        c.q[4 * i] = as_h2(qv.x);
+        c.q[4 * i + 1] = as_h2(qv.y);
+        c.q[4 * i + 2] = as_h2(qv.z);
+        c.q[4 * i + 3] = as_h2(qv.w);
     }
 
-    LaneState st;
+    LaneState<KV> st;
     st.m = kNegInf;
     st.l = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < E; ++i)
         st.acc[i] = 0.0f;
 
     const int32_t* table = P.block_tables + (int64_t)s * P.max_blocks_per_seq;
@@ -266,18 +327,18 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
         const int tok_hi = min(end, (chunk0 + kWave) * B);
         for (int t0 = tok_lo + wave * TILE; t0 < tok_hi; t0 += kWaves * TILE) {
             if (t0 + TILE <= end)
-                tile_step<D, B, false>(st, c, t0, ids, chunk0);
+                tile_step<KV, D, B, false>(st, c, t0, ids, chunk0);
             else
-                tile_step<D, B, true>(st, c, t0, ids, chunk0);
+                tile_step<KV, D, B, true>(st, c, t0, ids, chunk0);
         }
     }
 
     // Merge the lane groups of this wave (lanes l, l^LPT, l^2LPT, ...).
 #pragma unroll
     for (int off = LPT; off < kWave; off <<= 1) {
-        float acc_o[8];
+        float acc_o[E];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < E; ++i)
             acc_o[i] = __shfl_xor(st.acc[i], off);
         const float m_o = __shfl_xor(st.m, off);
         const float l_o = __shfl_xor(st.l, off);
@@ -289,8 +350,8 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
     __shared__ float s_m[kWaves], s_l[kWaves];
     if (lane < LPT) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            s_acc[wave][lane * 8 + i] = st.acc[i];
+        for (int i = 0; i < E; ++i)
+            s_acc[wave][lane * E + i] = st.acc[i];
     }
     if (lane == 0) {
         s_m[wave] = st.m;
@@ -311,6 +372,8 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
             o = fmaf(s_acc[w][d], wt, o);
         }
         o = o / L;
+        if constexpr (KV::kScaledOutput)
+            o *= P.v_scale;
         if (nparts_seq == 1) {
             P.out[row + d] = (_Float16)o;
         } else {
@@ -396,10 +459,10 @@ __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
     }
 }
 
-template <int D, int B>
+template <typename KV, int D, int B>
 hipError_t launch_decode(const DecodeParams& P, hipStream_t stream)
 {
-    hipLaunchKernelGGL((pa_partition_kernel<D, B>), dim3(P.total_units), dim3(kThreads), 0,
+    hipLaunchKernelGGL((pa_partition_kernel<KV, D, B>), dim3(P.total_units), dim3(kThreads), 0,
                        stream, P);
     if (P.num_partitions > 1)
         hipLaunchKernelGGL((pa_reduce_kernel<D>), dim3(P.num_seqs * P.num_heads), dim3(kThreads),
@@ -407,20 +470,32 @@ hipError_t launch_decode(const DecodeParams& P, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <typename KV>
+hipError_t dispatch(const DecodeParams& P, int head_dim, int block_size, hipStream_t stream)
+{
+    if (head_dim == 128 && block_size == 16)
+        return launch_decode<KV, 128, 16>(P, stream);
+    if (head_dim == 128 && block_size == 32)
+        return launch_decode<KV, 128, 32>(P, stream);
+    if (head_dim == 64 && block_size == 16)
+        return launch_decode<KV, 64, 16>(P, stream);
+    if (head_dim == 64 && block_size == 32)
+        return launch_decode<KV, 64, 32>(P, stream);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_decode_dispatch(const DecodeParams& P, int head_dim, int block_size,
                                   hipStream_t stream)
 {
-    if (head_dim == 128 && block_size == 16)
-        return launch_decode<128, 16>(P, stream);
-    if (head_dim == 128 && block_size == 32)
-        return launch_decode<128, 32>(P, stream);
-    if (head_dim == 64 && block_size == 16)
-        return launch_decode<64, 16>(P, stream);
-    if (head_dim == 64 && block_size == 32)
-        return launch_decode<64, 32>(P, stream);
-    return hipErrorInvalidValue;
+    return dispatch<KvF16>(P, head_dim, block_size, stream);
+}
+
+hipError_t launch_decode_fp8_dispatch(const DecodeParams& P, int head_dim, int block_size,
+                                      hipStream_t stream)
+{
+    return dispatch<KvFp8>(P, head_dim, block_size, stream);
 }
 
 }  // namespace pa

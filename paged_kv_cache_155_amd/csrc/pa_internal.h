@@ -10,8 +10,8 @@ namespace pa {
 struct DecodeParams {
     _Float16* out;
     const _Float16* q;
-    const _Float16* k_cache;
-    const _Float16* v_cache;
+    const void* k_cache;     // fp16 or FP8 codes, [NB, B, H, D]
+    const void* v_cache;
     const int32_t* block_tables;
     const int32_t* context_lens;
     float* ws_o;  // [S, H, NP, D] normalised partition rows
@@ -23,11 +23,20 @@ struct DecodeParams {
     int32_t partition_size;  // tokens per partition (the whole table when not split)
     int32_t num_partitions;  // NP = ceil(max_blocks_per_seq * block_size / partition_size)
     uint32_t total_units;    // num_seqs * num_heads * num_partitions workgroups
-    float scale_log2;        // scale * log2(e)
+    float scale_log2;        // scale * log2(e) (times the K scale for FP8)
+    float v_scale;           // FP8: dequantisation scale of V (unused for fp16)
 };
 
 hipError_t launch_decode_dispatch(const DecodeParams& p, int head_dim, int block_size,
                                   hipStream_t stream);
+
+hipError_t launch_decode_fp8_dispatch(const DecodeParams& p, int head_dim, int block_size,
+                                      hipStream_t stream);
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                        void* v_cache, const int64_t* slot_mapping,
+                                        int32_t num_tokens, int64_t num_slots, int32_t row_elems,
+                                        float k_inv_scale, float v_inv_scale, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
                                     void* v_cache, const int64_t* slot_mapping, int32_t num_tokens,

@@ -329,3 +329,41 @@ def make_random(context_lens, num_heads, head_dim, block_size, seed=0, partition
         scale=np.float32(1.0 / math.sqrt(D)), q=q, k_cache=k_cache, v_cache=v_cache,
         block_tables=tables, context_lens=lens.astype(np.int32), key=key, value=value,
         slot_mapping=slots, poison_block=poison_block, ref_counts=ref)
+
+
+@dataclasses.dataclass
+class Fp8Pools:
+    """FP8 (OCP E4M3) copies of a workload's K/V pools."""
+    k_cache: np.ndarray   # [NB, B, H, D] uint8 codes
+    v_cache: np.ndarray
+    k_scale: np.float32
+    v_scale: np.float32
+
+
+def fp8_pools(w, headroom=1.0):
+    """Quantise a workload's pools for the FP8 cache variant: one scale per
+    cache, scale = amax(|pool and new tokens|) / 448 (the largest E4M3 value,
+    so nothing saturates), codes from torch's float -> float8_e4m3fn cast of
+    x * (1/scale) on the host.  These are *inputs*: any valid codes with a
+    realistic spread will do; never-read NaN slots stay NaN codes."""
+    import torch
+
+    def scale_of(a, b):
+        amax = max(float(np.nanmax(np.abs(a.astype(np.float32)))) if a.size else 0.0,
+                   float(np.nanmax(np.abs(b.astype(np.float32)))) if b.size else 0.0)
+        return np.float32(max(amax, 1e-6) * headroom / 448.0)
+
+    def quant(a, scale):
+        inv = np.float32(1.0 / float(scale))
+        t = torch.from_numpy(a.reshape(-1))
+        out = torch.empty(t.numel(), dtype=torch.uint8)
+        step = 1 << 24
+        for i in range(0, t.numel(), step):
+            y = t[i:i + step].float() * float(inv)
+            out[i:i + step] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+        return out.numpy().reshape(a.shape)
+
+    ks = scale_of(w.k_cache, w.key)
+    vs = scale_of(w.v_cache, w.value)
+    return Fp8Pools(k_cache=quant(w.k_cache, ks), v_cache=quant(w.v_cache, vs), k_scale=ks,
+                    v_scale=vs)

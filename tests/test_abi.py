@@ -50,7 +50,8 @@ def test_workspace_size(lib):
 
 
 P = ctypes.c_void_p
-FAKE = P(0x10000)  # never dereferenced: every call below fails validation first
+FAKE = P(0x10000)  # never dereferenced: every call in this file fails validation first
+# (or has nothing to do), so nothing is ever launched from these tests
 
 
 def _decode(lib, **kw):
@@ -102,3 +103,24 @@ def test_copy_and_swap_reject(lib):
     assert g(FAKE, P(0), mp, 2, 8, 16, 4096, None) == -1
     m2 = np.array([[-1, 0]], dtype=np.int64)
     assert g(FAKE, FAKE, m2.ctypes.data_as(ctypes.c_void_p), 1, 8, 16, 4096, None) == -8
+
+
+def test_fp8_rejects(lib):
+    f = lib.pa_reshape_and_cache_fp8
+    f.argtypes = [P, P, P, P, P] + [ctypes.c_int32] * 5 + [ctypes.c_float, ctypes.c_float, P]
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 8, 16, 0.0, 1.0, None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 8, 16, 1.0, float("inf"), None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 24, 8, 16, 1.0, 1.0, None) == -3
+    assert f(FAKE, P(0), FAKE, FAKE, FAKE, 2, 4, 128, 8, 16, 1.0, 1.0, None) == -1
+    g = lib.pa_decode_fp8
+    # every call below must fail validation: the pointers are fake
+    args = [FAKE] * 6 + [2, 4, 128, 8, 16, 4, 0.088, 0.01, 0.01, 0, P(0), 0, None]
+    bad = list(args)
+    bad[13] = -1.0  # k_scale
+    assert g(*bad) == -2
+    bad = list(args)
+    bad[8] = 96     # head_dim
+    assert g(*bad) == -3
+    bad = list(args)
+    bad[15] = 24    # partition size
+    assert g(*bad) == -4

@@ -1,0 +1,116 @@
+"""FP8 (OCP E4M3) KV cache: the quantising reshape_and_cache is bit-exact
+against the oracle's quantiser (every fp16 bit pattern, several scales), the
+hardware decode of every code is exact, and pa_decode_fp8 matches the oracle
+on the workloads (pools quantised on the host as inputs) and on a length
+sweep."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_close, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_fp8(orc, w, P=None, pools=None):
+    """GPU: quantising write + FP8 decode; oracle: the same on the same bytes."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import fp8_pools
+    f = pools or fp8_pools(w)
+    P = w.partition_size if P is None else P
+    kc, vc = to_dev(f.k_cache), to_dev(f.v_cache)
+    q = to_dev(w.q)
+    bt, cl = to_dev(w.block_tables), to_dev(w.context_lens)
+    out = torch.full_like(q, float("nan"))
+    pa.reshape_and_cache_fp8(to_dev(w.key), to_dev(w.value), kc, vc, to_dev(w.slot_mapping),
+                             f.k_scale, f.v_scale)
+    pa.decode_fp8(out, q, kc, vc, bt, cl, float(w.scale), f.k_scale, f.v_scale, partition_size=P)
+    torch.cuda.synchronize()
+    hk, hv = f.k_cache.copy(), f.v_cache.copy()
+    orc.reshape_and_cache_fp8(w.key, w.value, hk, hv, w.slot_mapping, f.k_scale, f.v_scale)
+    assert np.array_equal(kc.cpu().numpy(), hk), "FP8 K pool differs after the write"
+    assert np.array_equal(vc.cpu().numpy(), hv), "FP8 V pool differs after the write"
+    ref = orc.decode_fp8(w.q, hk, hv, w.block_tables, w.context_lens, float(w.scale), f.k_scale,
+                         f.v_scale)
+    return out.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.02, 50.0, 1.0 / 512])
+def test_quantiser_every_fp16_pattern(orc, scale):
+    """All 65,536 fp16 bit patterns (NaN, +-Inf, subnormals, +-0 included)
+    through the quantising write, at scales that push values into the E4M3
+    saturation and subnormal ranges."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    log(f"[fp8] quantiser on every fp16 pattern, scale {scale}")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    key = bits.view(np.float16).reshape(16, 32, 128)
+    value = (bits ^ 0x8000).astype(np.uint16).view(np.float16).reshape(16, 32, 128)
+    NB, B = 4, 16
+    kc = to_dev(np.full((NB, B, 32, 128), 0xA5, dtype=np.uint8))
+    vc = to_dev(np.full((NB, B, 32, 128), 0x5A, dtype=np.uint8))
+    slots = np.array([3, 17, 0, 63, 5, 40, 41, 42, 1, 2, 20, 21, 30, 31, 50, 60], dtype=np.int64)
+    pa.reshape_and_cache_fp8(to_dev(key), to_dev(value), kc, vc, to_dev(slots), scale, scale)
+    torch.cuda.synchronize()
+    hk = np.full((NB, B, 32, 128), 0xA5, dtype=np.uint8)
+    hv = np.full((NB, B, 32, 128), 0x5A, dtype=np.uint8)
+    orc.reshape_and_cache_fp8(key, value, hk, hv, slots, scale, scale)
+    gk, gv = kc.cpu().numpy(), vc.cpu().numpy()
+    bad = np.flatnonzero(gk.reshape(-1) != hk.reshape(-1))
+    assert bad.size == 0, f"{bad.size} K codes differ, first at {bad[:5]}"
+    assert np.array_equal(gv, hv)
+
+
+def test_every_code_decodes_exactly():
+    """ctx = 1 and v_scale = 1: the output is value(code) exactly (every E4M3
+    value is an fp16 value), for all 254 non-NaN codes placed in V."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    log("[fp8] exact decode of every code")
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    H, D = 2, 128
+    v = np.zeros(H * D, dtype=np.uint8)
+    v[:codes.size] = codes
+    kc = np.zeros((2, 16, H, D), dtype=np.uint8)
+    vc = np.zeros((2, 16, H, D), dtype=np.uint8)
+    vc[1, 0] = v.reshape(H, D)
+    q = to_dev(np.ones((1, H, D), dtype=np.float16))
+    out = torch.empty_like(q)
+    pa.decode_fp8(out, q, to_dev(kc), to_dev(vc), to_dev(np.array([[1]], np.int32)),
+                  to_dev(np.array([1], np.int32)), 0.1, 1.0, 1.0, partition_size=0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1)[:codes.size].astype(np.float64)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(got, ref)
+
+
+SMALL = [(0, None, {}), (1, None, dict(num_seqs=16, num_heads=4)),
+         (2, 32, dict(num_seqs=24, num_heads=3)), (3, None, dict(num_seqs=12, num_heads=2)),
+         (4, None, dict(num_seqs=2, num_heads=2))]
+FULL = [(1, None, {}), (2, 16, {}), (3, None, {}), (4, None, {})]
+
+
+@pytest.mark.parametrize("cfg,bs,kw", SMALL + FULL,
+                         ids=[f"c{c}_B{b or 'd'}_{'small' if kw else 'full'}" for c, b, kw in SMALL + FULL])
+def test_fp8_parity(orc, cfg, bs, kw):
+    from paged_kv_cache_155_amd.workloads import make_workload
+    w = make_workload(cfg, block_size=bs, **kw)
+    log(f"[fp8] parity config {cfg} B={w.block_size} S={w.num_seqs} H={w.num_heads}")
+    got, ref = _run_fp8(orc, w)
+    ea, er = assert_close(got, ref, f"fp8 config {cfg}")
+    log(f"[fp8] config {cfg}: max abs err {ea:.3e}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("P", [0, 32, 512])
+def test_fp8_length_sweep(orc, D, B, P):
+    from paged_kv_cache_155_amd.workloads import make_random
+    lens = sorted(set(list(range(0, 3 * B + 2)) + [63, 64, 65, 127, 128, 129, 255, 256, 257, 511,
+                                                   512, 513, 1025, 2049]))
+    log(f"[fp8] length sweep D={D} B={B} P={P}")
+    w = make_random(lens, 2, D, B, seed=5000 + D + B + P, partition_size=P)
+    got, ref = _run_fp8(orc, w, P=P)
+    assert_close(got, ref, f"fp8 sweep D={D} B={B} P={P}")
+    zero = np.flatnonzero(w.context_lens == 0)
+    assert not got[zero].any()
