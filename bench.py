@@ -41,6 +41,8 @@ def _args():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--kv-dtype", choices=["fp16", "fp8"], default="fp16",
+                    help="cache element type: fp16, or FP8 (OCP E4M3, one scale per cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=float, default=1.0e7,
                     help="cap on token-heads of oracle work in the CPU baseline sample")
@@ -235,7 +237,15 @@ def main():
     def up(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
-    q, kc, vc = up(w.q), up(w.k_cache), up(w.v_cache)
+    fp8 = a.kv_dtype == "fp8"
+    if fp8:
+        from paged_kv_cache_155_amd.workloads import fp8_pools
+        f8 = fp8_pools(w)
+        kc, vc = up(f8.k_cache), up(f8.v_cache)
+        ks, vs = float(f8.k_scale), float(f8.v_scale)
+    else:
+        kc, vc = up(w.k_cache), up(w.v_cache)
+    q = up(w.q)
     bt, cl = up(w.block_tables), up(w.context_lens)
     key, val, slots = up(w.key), up(w.value), up(w.slot_mapping)
     out = torch.empty_like(q)
@@ -244,9 +254,21 @@ def main():
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     scale = float(w.scale)
 
+    def write():
+        if fp8:
+            pa.reshape_and_cache_fp8(key, val, kc, vc, slots, ks, vs)
+        else:
+            pa.reshape_and_cache(key, val, kc, vc, slots)
+
+    def attend():
+        if fp8:
+            pa.decode_fp8(out, q, kc, vc, bt, cl, scale, ks, vs, partition_size=P, workspace=ws)
+        else:
+            pa.decode(out, q, kc, vc, bt, cl, scale, partition_size=P, workspace=ws)
+
     def step():
-        pa.reshape_and_cache(key, val, kc, vc, slots)
-        pa.decode(out, q, kc, vc, bt, cl, scale, partition_size=P, workspace=ws)
+        write()
+        attend()
 
     for _ in range(a.warmup):
         step()
@@ -262,9 +284,9 @@ def main():
     t_begin.record(stream)
     for i in range(K):
         ev[i][0].record(stream)
-        pa.reshape_and_cache(key, val, kc, vc, slots)
+        write()
         ev[i][1].record(stream)
-        pa.decode(out, q, kc, vc, bt, cl, scale, partition_size=P, workspace=ws)
+        attend()
         ev[i][2].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -275,19 +297,21 @@ def main():
     ms_step = total_ms / K
     t_dec = float(np.mean(dec_ms))
     t_rc = float(np.mean(rc_ms))
-    kvb = w.kv_bytes()
+    kvb = w.kv_bytes() // 2 if fp8 else w.kv_bytes()
     achieved = kvb / (t_dec * 1e-3) / 1e9
     value = kvb / (ms_step * 1e-3) / 1e9
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": a.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3" if fp8 else "f16",
+        "data": "synthetic",
         "config": {
             "workload": f"config{a.config}: {DESCRIPTIONS[a.config]}",
             "num_seqs": w.num_seqs, "num_heads": w.num_heads, "head_dim": w.head_dim,
             "block_size": w.block_size, "partition_size": P, "num_blocks": w.num_blocks,
-            "kv_bytes_per_step": kvb, "unique_kv_bytes": w.unique_kv_bytes(),
+            "kv_dtype": a.kv_dtype, "kv_bytes_per_step": kvb,
+            "unique_kv_bytes": w.unique_kv_bytes() // (2 if fp8 else 1),
             "decode_tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
             "decode_only_tokens_per_s_per_layer": round(w.num_seqs / (t_dec * 1e-3), 1),
             "t_decode_us_mean": round(t_dec * 1e3, 2),
@@ -297,11 +321,12 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic(f"config{a.config}_B{w.block_size}_P{P}"),
-                     "kernel": "pa_decode (partition kernel + reduce kernel), HIP events"},
+                     "traffic": None if fp8 else _traffic(f"config{a.config}_B{w.block_size}_P{P}"),
+                     "kernel": ("pa_decode_fp8" if fp8 else "pa_decode")
+                               + " (partition kernel + reduce kernel), HIP events"},
         "cpu_baseline": None,
     }
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and not fp8:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens, a.cpu_repeats)
     print(json.dumps(line), flush=True)
 
