@@ -67,6 +67,8 @@ class Oracle:
                                                 + [ctypes.c_double, ctypes.c_float, ctypes.c_float,
                                                    _P])
         lib.oracle_decode_fp8_pairs.restype = ctypes.c_int
+        lib.oracle_prefill.argtypes = [_P] * 7 + [_I32] * 7 + [ctypes.c_double, _P]
+        lib.oracle_prefill.restype = ctypes.c_int
         self.lib = lib
         self.threads_used = 1
 
@@ -227,6 +229,27 @@ class Oracle:
             raise ValueError(f"oracle_decode_fp8_pairs failed ({rc})")
         self.threads_used = int(used[0])
         return out.reshape(S, H, D) if whole else out
+
+    # -- multi-query (chunked prefill) ------------------------------------------
+    def prefill(self, q, k_cache, v_cache, block_tables, context_lens, query_start, scale):
+        """fp64 [T, H, D]: causal attention of each sequence's last n_s positions."""
+        q, k_cache, v_cache = _u16(q), _u16(k_cache), _u16(v_cache)
+        T, H, D = q.shape
+        nb, bs, nh, hd = k_cache.shape
+        assert (nh, hd) == (H, D) and v_cache.shape == k_cache.shape
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        qs = np.ascontiguousarray(query_start, dtype=np.int32)
+        S = cl.shape[0]
+        out = np.zeros((T, H, D), dtype=np.float64)
+        used = np.zeros(1, dtype=np.int32)
+        rc = self.lib.oracle_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
+                                     _ptr(cl), _ptr(qs), S, T, H, D, nb, bs, bt.shape[1],
+                                     float(scale), _ptr(used))
+        if rc:
+            raise ValueError(f"oracle_prefill failed ({rc})")
+        self.threads_used = int(used[0])
+        return out
 
 
 _default = None

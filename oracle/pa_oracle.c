@@ -24,6 +24,8 @@
  *   [arch] "vLLM基础架构：核心组件、PagedAttention原理、KV Cache管理与连续批处理机制"
  *          §2.3  shared blocks are copied before a sequence writes into one
  *                (copy-on-write), then its table points at the copy
+ *          §4.3  prefill and decode requests may share one batch
+ *   [eng]  §4.2 a batch mixes requests in prefill with requests in decode
  *   [src]  "【硬核】啃透vLLM源码：从PagedAttention到连续批处理，大模型推理加速24倍的秘密"
  *          §三   blocks are swapped out to host memory and back in
  *
@@ -513,6 +515,83 @@ int oracle_decode_fp8_pairs(double *out, const int32_t *pairs, int32_t num_pairs
             load_query(qbuf, q, s, h, num_heads, head_dim);
             attend_contiguous(out + (int64_t)p * head_dim, qbuf, Kbuf, Vbuf, L, head_dim, scale,
                               logits);
+        }
+        if (local) {
+#pragma omp critical
+            status = local;
+        }
+        free(Kbuf);
+        free(Vbuf);
+        free(qbuf);
+        free(logits);
+    }
+    if (threads_used)
+        *threads_used = nthreads;
+    return status;
+}
+
+/* ---------------------------------------------------------------------------
+ * Multi-query paged attention ([10x] §4.3 and [eng] §4.2: prefill and
+ * decode work in one batch).  Reading: sequence s brings n_s = query_start[s+1] - query_start[s]
+ * query rows, the last n_s positions of its context (their K/V are already
+ * in the cache); row i sits at logical position p = context_lens[s] - n_s + i
+ * and attends positions 0..p (causal).  n_s = 1 is the decode step.
+ * q and out are [num_tokens, num_heads, head_dim] with the rows of sequence s
+ * at query_start[s] .. query_start[s+1]-1.
+ * ------------------------------------------------------------------------- */
+int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
+                   const uint16_t *v_cache, const int32_t *block_tables,
+                   const int32_t *context_lens, const int32_t *query_start, int32_t num_seqs,
+                   int32_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                   int32_t block_size, int32_t max_blocks_per_seq, double scale,
+                   int32_t *threads_used)
+{
+    int rc = check_shapes(num_seqs, num_heads, head_dim, num_blocks, block_size,
+                          max_blocks_per_seq);
+    if (rc)
+        return rc;
+    if (query_start[0] != 0 || query_start[num_seqs] != num_tokens)
+        return OR_ERR_ARG;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int32_t n = query_start[s + 1] - query_start[s];
+        if (n < 0 || n > context_lens[s])
+            return OR_ERR_RANGE;
+    }
+    int64_t max_len = (int64_t)max_blocks_per_seq * block_size;
+    int status = OR_OK;
+    int nthreads = 1;
+    int64_t units = (int64_t)num_seqs * num_heads;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        nthreads = omp_get_num_threads();
+#endif
+        double *Kbuf = malloc(sizeof(double) * (size_t)(max_len * head_dim + 1));
+        double *Vbuf = malloc(sizeof(double) * (size_t)(max_len * head_dim + 1));
+        double *qbuf = malloc(sizeof(double) * (size_t)head_dim);
+        double *logits = malloc(sizeof(double) * (size_t)(max_len + 1));
+        int local = (Kbuf && Vbuf && qbuf && logits) ? OR_OK : OR_ERR_NOMEM;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < units; ++u) {
+            if (local)
+                continue;
+            int32_t s = (int32_t)(u / num_heads), h = (int32_t)(u % num_heads);
+            int L = oracle_gather(Kbuf, Vbuf, k_cache, v_cache, block_tables, context_lens, s, h,
+                                  num_heads, head_dim, num_blocks, block_size,
+                                  max_blocks_per_seq);
+            if (L < 0) {
+                local = L;
+                continue;
+            }
+            int32_t n = query_start[s + 1] - query_start[s];
+            for (int32_t i = 0; i < n; ++i) {
+                int32_t row = query_start[s] + i;
+                int32_t visible = L - n + i + 1; /* positions 0 .. L-n+i */
+                load_query(qbuf, q, row, h, num_heads, head_dim);
+                attend_contiguous(out + ((int64_t)row * num_heads + h) * head_dim, qbuf, Kbuf, Vbuf,
+                                  visible, head_dim, scale, logits);
+            }
         }
         if (local) {
 #pragma omp critical

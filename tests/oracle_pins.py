@@ -22,6 +22,10 @@ What pins what:
   copy / swap      numpy block assignment on random bit patterns; a
                    copy-on-write sequence ("vLLM基础架构" §2.3) seen through
                    the gather; out-of-range pairs
+  multi-query      one query per sequence reduces bitwise to the decode;
+                   torch SDPA with the causal mask of the last n positions on
+                   the contiguous layout (n = ctx is the ordinary causal
+                   mask); pure-Python brute force on tiny inputs
   FP8 (OCP E4M3)   all 256 codes vs torch.float8_e4m3fn; the encoder vs
                    torch's float -> float8_e4m3fn cast wherever torch does not
                    overflow (all fp16 values, ties, random floats), closed forms
@@ -477,11 +481,89 @@ def pin_fp8_reshape(orc):
     assert np.array_equal(kc.reshape(NB * B, H, D), rk) and np.array_equal(vc.reshape(NB * B, H, D), rv)
 
 
+def _prefill_case(rng, lens, nq, H, D, B, identity=False):
+    S = len(lens)
+    MB = max(1, max(-(-int(L) // B) for L in lens))
+    if identity:
+        bt = (np.arange(S)[:, None] * MB + np.arange(MB)[None, :]).astype(np.int32)
+        NB = S * MB
+    else:
+        NB = sum(-(-int(L) // B) for L in lens) + 2
+        perm = rng.permutation(NB)
+        bt = np.full((S, MB), perm[-1], dtype=np.int32)
+        c = 0
+        for s_, L in enumerate(lens):
+            n = -(-int(L) // B)
+            bt[s_, :n] = perm[c:c + n]
+            c += n
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = _f16(rng.standard_normal((int(qs[-1]), H, D)))
+    kc = _f16(rng.standard_normal((NB, B, H, D)))
+    vc = _f16(rng.standard_normal((NB, B, H, D)))
+    return q, kc, vc, bt, np.asarray(lens, np.int32), qs, MB
+
+
+def pin_prefill_single_query_is_decode(orc):
+    rng = np.random.default_rng(14)
+    q, kc, vc, bt, cl, qs, _ = _prefill_case(rng, [1, 30, 77, 16], [1, 1, 1, 1], 2, 64, 16)
+    a = orc.prefill(q, kc, vc, bt, cl, qs, 0.125)
+    b = orc.decode(q, kc, vc, bt, cl, 0.125)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def pin_prefill_sdpa_causal(orc):
+    import torch
+    rng = np.random.default_rng(15)
+    lens, nq = [37, 64, 5, 50], [37, 9, 1, 16]   # first: a whole prompt; others: chunks
+    H, D, B = 2, 64, 16
+    q, kc, vc, bt, cl, qs, MB = _prefill_case(rng, lens, nq, H, D, B, identity=True)
+    got = orc.prefill(q, kc, vc, bt, cl, qs, 0.125)
+    for s in range(len(lens)):
+        L, n = lens[s], nq[s]
+        Kc = torch.from_numpy(kc[s * MB:(s + 1) * MB].reshape(MB * B, H, D)[:L].astype(np.float64))
+        Vc = torch.from_numpy(vc[s * MB:(s + 1) * MB].reshape(MB * B, H, D)[:L].astype(np.float64))
+        Q = torch.from_numpy(q[qs[s]:qs[s + 1]].astype(np.float64))
+        allowed = torch.arange(L)[None, :] <= (L - n + torch.arange(n))[:, None]
+        for h in range(H):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                Q[:, h].reshape(1, n, D).contiguous(), Kc[:, h].reshape(1, L, D).contiguous(),
+                Vc[:, h].reshape(1, L, D).contiguous(), attn_mask=allowed.reshape(1, n, L),
+                scale=0.125).reshape(n, D).numpy()
+            assert np.allclose(got[qs[s]:qs[s + 1], h], ref, rtol=1e-11, atol=1e-13), (s, h)
+        if n == L:
+            causal = torch.nn.functional.scaled_dot_product_attention(
+                Q[:, 0].reshape(1, n, D).contiguous(), Kc[:, 0].reshape(1, L, D).contiguous(),
+                Vc[:, 0].reshape(1, L, D).contiguous(), is_causal=True, scale=0.125).reshape(n, D)
+            assert np.allclose(got[qs[s]:qs[s + 1], 0], causal.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def pin_prefill_brute_force(orc):
+    rng = np.random.default_rng(16)
+    for B in (2, 4):
+        lens, nq = [3, 9, 6], [3, 4, 1]
+        q, kc, vc, bt, cl, qs, _ = _prefill_case(rng, lens, nq, 1, 8, B)
+        got = orc.prefill(q, kc, vc, bt, cl, qs, 0.5)
+        for s in range(3):
+            L, n = lens[s], nq[s]
+            for i in range(n):
+                p = L - n + i
+                rows = [(kc[bt[s][t // B]][t % B][0].astype(float).tolist(),
+                         vc[bt[s][t // B]][t % B][0].astype(float).tolist()) for t in range(p + 1)]
+                qq = q[qs[s] + i][0].astype(float).tolist()
+                lg = [0.5 * math.fsum(a * b for a, b in zip(qq, k)) for k, _ in rows]
+                mx = max(lg)
+                e = [math.exp(x - mx) for x in lg]
+                z = math.fsum(e)
+                ref = [math.fsum(w * v[d] for w, (_, v) in zip(e, rows)) / z for d in range(8)]
+                assert np.allclose(got[qs[s] + i, 0], ref, rtol=1e-11, atol=1e-13), (B, s, i)
+
+
 PINS = [pin_half_decode_exhaustive, pin_gather_worked_example, pin_contiguous_sdpa,
         pin_block_permutation_invariance, pin_brute_force_tiny, pin_closed_forms, pin_needles,
         pin_reshape_scatter, pin_reshape_worked_example, pin_copy_blocks, pin_copy_on_write,
         pin_swap_blocks, pin_e4m3_decode_exhaustive, pin_e4m3_encode, pin_quantize_scale,
-        pin_fp8_decode_sdpa, pin_fp8_reshape]
+        pin_fp8_decode_sdpa, pin_fp8_reshape, pin_prefill_single_query_is_decode,
+        pin_prefill_sdpa_causal, pin_prefill_brute_force]
 
 
 def main(argv):

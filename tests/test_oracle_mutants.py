@@ -70,6 +70,11 @@ MUTANTS = {
     "fp8_reshape_value_k_scale": ("oracle_quantize_e4m3(value + t * row, v_cache + slot * row, row, v_scale);",
                                   "oracle_quantize_e4m3(value + t * row, v_cache + slot * row, row, k_scale);"),
     "fp8_quantize_scale_not_inverted": ("float y = xf * inv;", "float y = xf * scale;"),
+    "prefill_excludes_self": ("int32_t visible = L - n + i + 1;", "int32_t visible = L - n + i;"),
+    "prefill_positions_from_zero": ("int32_t visible = L - n + i + 1;", "int32_t visible = i + 1;"),
+    "prefill_sees_everything": ("int32_t visible = L - n + i + 1;", "int32_t visible = L;"),
+    "prefill_rows_reversed": ("int32_t row = query_start[s] + i;",
+                              "int32_t row = query_start[s + 1] - 1 - i;"),
 }
 
 
