@@ -48,9 +48,12 @@ def _args():
                     help="cap on token-heads of oracle work in the CPU baseline sample")
     ap.add_argument("--cpu-repeats", type=int, default=3,
                     help="oracle runs over the sample (the median is reported)")
-    ap.add_argument("--op", choices=["step", "copy_blocks", "swap"], default="step",
+    ap.add_argument("--op", choices=["step", "copy_blocks", "swap", "cascade", "multi_query"],
+                    default="step",
                     help="step: the decode step (default); copy_blocks / swap: the block "
-                         "copy-on-write and GPU<->host swap entry points on config 1's pool")
+                         "copy-on-write and GPU<->host swap entry points on config 1's pool; "
+                         "cascade: the shared-prefix step through pa_decode_cascade (config "
+                         "3); multi_query: a chunked-prefill batch through pa_multi_query")
     ap.add_argument("--pairs", type=int, default=1024, help="blocks per copy/swap call")
     ap.add_argument("--probe", choices=["copy"], default=None)
     ap.add_argument("--probe-mib", type=int, default=1024)
@@ -169,6 +172,94 @@ def bench_blocks(op, pairs, iters):
         print(json.dumps(ln), flush=True)
 
 
+MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+
+
+def bench_cascade(iters, warmup):
+    """Shared-prefix step (config 3) with the prefix read once per 16
+    sequences: reshape_and_cache + pa_decode_cascade."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import DESCRIPTIONS, make_workload, split_shared_prefix
+    w = make_workload(3, poison=False)
+    prefix, plen, st, sl = split_shared_prefix(w, 32)
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    kc, vc, q = up(w.k_cache), up(w.v_cache), up(w.q)
+    key, val, slots = up(w.key), up(w.value), up(w.slot_mapping)
+    pt, stt, slt = up(prefix), up(st), up(sl)
+    out = torch.empty_like(q)
+    P = 0
+    ws = torch.empty(pa.decode_cascade_workspace_size(w.num_seqs, w.num_heads, w.head_dim,
+                                                      w.block_size, plen, st.shape[1], P),
+                     dtype=torch.uint8, device="cuda")
+    scale = float(w.scale)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        pa.reshape_and_cache(key, val, kc, vc, slots)
+        pa.decode_cascade(out, q, kc, vc, pt, plen, stt, slt, scale, P, ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        pa.reshape_and_cache(key, val, kc, vc, slots)
+        e[1].record(stream)
+        pa.decode_cascade(out, q, kc, vc, pt, plen, stt, slt, scale, P, ws)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / iters
+    dec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    rc = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    uniq, logical = w.unique_kv_bytes(), w.kv_bytes()
+    print(json.dumps({
+        "op": "cascade", "workload": f"config3: {DESCRIPTIONS[3]}", "partition_size": P,
+        "t_decode_us_mean": round(dec * 1e3, 2), "t_reshape_us_mean": round(rc * 1e3, 2),
+        "wall_ms_per_step": round(step_ms, 4),
+        "decode_tokens_per_s_per_layer": round(w.num_seqs / ((dec + rc) * 1e-3), 1),
+        "kv_bytes_logical": logical, "kv_bytes_unique": uniq,
+        "roofline": {"bound": "hbm", "achieved": round(uniq / (dec * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(uniq / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes": "unique K/V bytes"},
+        "logical_kv_gbs": round(logical / (dec * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def bench_multi_query(iters, warmup):
+    """A chunked-prefill batch: 16 sequences of 2048 positions whose last 512
+    are this step's new tokens (32 heads x 128, B = 16)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import make_multi_query
+    S, ctx, n = 16, 2048, 512
+    w, qh, qs = make_multi_query([ctx] * S, [n] * S, 32, 128, 16, seed=155, poison=False)
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    kc, vc, q = up(w.k_cache), up(w.v_cache), up(qh)
+    bt, cl, qst = up(w.block_tables), up(w.context_lens), up(qs)
+    out = torch.empty_like(q)
+    scale = float(w.scale)
+    ms = _time_events(lambda: pa.multi_query(out, q, kc, vc, bt, cl, qst, n, scale), iters,
+                      warmup)
+    t = float(np.median(ms)) * 1e-3
+    H, D = w.num_heads, w.head_dim
+    visible = sum(ctx - n + i + 1 for i in range(n)) * S          # (row, key) pairs per head
+    flops = 4.0 * D * visible * H                                   # q.k and p.v
+    kv_unique = S * ctx * H * D * 2 * 2
+    print(json.dumps({
+        "op": "multi_query", "workload": f"{S} seqs x {ctx} positions, last {n} new, 32 heads x 128",
+        "rows": S * n, "us_median": round(t * 1e6, 2),
+        "query_tokens_per_s": round(S * n / t, 1),
+        "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 2),
+                     "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / t / 1e12 / MFMA_F16_TFLOPS, 4)},
+        "kv_unique_gbs": round(kv_unique / t / 1e9, 1)}), flush=True)
+
+
 def cpu_baseline(w, sample_tokens, repeats):
     """Time the oracle (as it stands) on a bounded, deterministic sample of
     (sequence, head) pairs of the same workload (the whole workload when it
@@ -224,6 +315,12 @@ def main():
     pa.load()
     if a.probe == "copy":
         probe_copy(a.probe_mib)
+        return
+    if a.op == "cascade":
+        bench_cascade(a.steps, a.warmup)
+        return
+    if a.op == "multi_query":
+        bench_multi_query(a.steps, a.warmup)
         return
     if a.op != "step":
         bench_blocks(a.op, a.pairs, a.steps)

@@ -7,10 +7,12 @@
  *          §2.1 attention equation; §2.3 paged attention equations and the
  *          gather K_paged[i] = K_physical[BlockTable[i / B]][i mod B];
  *          §4.2 cache layout [num_blocks, block_size, num_heads, head_size];
- *          §3.3 FP8 quantisation (named only)
+ *          §3.3 FP8 quantisation (named only); §4.3 prefill and decode work
+ *          in one batch; §4.4 requests sharing a prefix reuse its blocks
  *   [eng]  "深入解析LLM推理引擎：从PagedAttention到调度优化"
- *          §3.2 on-demand block filling and the block table; §3.3 the gather
- *          driven by block_table and the current position
+ *          §3.2 on-demand block filling, the block table, shared prefix
+ *          blocks; §3.3 the gather driven by block_table and the current
+ *          position; §4.2 batches that mix prefill and decode requests
  *   [arch] "vLLM基础架构：核心组件、PagedAttention原理、KV Cache管理与连续批处理机制"
  *          §2.3 a new block every block_size tokens; shared prefix blocks;
  *          copy-on-write of a shared block before a sequence writes into it
@@ -134,6 +136,62 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
               int32_t max_blocks_per_seq, float scale, int32_t partition_size,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode for a batch whose sequences all begin with the same shared prefix
+ * ([eng] §3.2, [10x] §4.4: several tables list the same physical blocks).
+ * The result equals pa_decode over the tables prefix_block_table ++
+ * block_tables[s] with context prefix_len + context_lens[s]; it is computed
+ * so that the prefix is read once per 16 sequences and head (matrix-core
+ * passes of 16 queries against 64-token pieces of the prefix) and each
+ * suffix once, all pieces merged with the log-sum-exp identity.
+ *
+ *   prefix_block_table  int32 [prefix_len / block_size], DEVICE: the prefix's
+ *                       physical blocks in logical order
+ *   prefix_len          tokens in the prefix, a multiple of block_size
+ *                       (0: plain pa_decode)
+ *   block_tables,
+ *   context_lens        the private suffixes: [num_seqs, max_blocks_per_seq]
+ *                       and [num_seqs] (suffix lengths, 0 allowed)
+ *   workspace           at least pa_decode_cascade_workspace_size(...) bytes
+ * Other arguments, layouts and errors as pa_decode.  head_dim 64 or 128,
+ * block_size 16 or 32.
+ */
+size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t prefix_len,
+                                        int32_t max_blocks_per_seq, int32_t partition_size);
+
+int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* prefix_block_table, int32_t prefix_len,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                      int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Multi-query paged attention: several new tokens per sequence in one batch
+ * (chunked prefill, or prefill mixed with decode: [10x] §4.3, [eng] §4.2).
+ * Sequence s brings n_s = query_start[s+1] - query_start[s] query rows; they
+ * are the last n_s positions of its context (their K/V already written, e.g.
+ * by pa_reshape_and_cache), so row i sits at logical position
+ * p = context_lens[s] - n_s + i and attends positions 0..p (causal):
+ *   out[row, h, :] = softmax(scale * q[row, h, :] . K_paged[s, h, 0..p]^T)
+ *                    . V_paged[s, h, 0..p, :]
+ * n_s = 1 is the decode step.
+ *
+ *   q, out         fp16 [num_tokens, num_heads, head_dim]; the rows of
+ *                  sequence s are query_start[s] .. query_start[s+1]-1
+ *   query_start    int32 [num_seqs + 1], DEVICE, non-decreasing,
+ *                  query_start[0] = 0, query_start[num_seqs] = num_tokens
+ *   max_query_len  an upper bound of every n_s (sizes the launch)
+ *   block_tables, context_lens  as pa_decode; n_s <= context_lens[s]
+ * head_dim 64 or 128, block_size 16 or 32.  No workspace.
+ */
+int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                   int32_t max_query_len, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                   int32_t block_size, int32_t max_blocks_per_seq, float scale, void* stream);
 
 /*
  * FP8 KV cache.  [10x] §3.3 names FP8 quantisation without fixing a format;

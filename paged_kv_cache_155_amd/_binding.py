@@ -50,6 +50,13 @@ def load(path=None):
     lib.pa_decode_fp8.argtypes = ([_P] * 6 + [_I32] * 6 + [ctypes.c_float] * 3
                                   + [_I32, _P, ctypes.c_size_t, _P])
     lib.pa_decode_fp8.restype = ctypes.c_int
+    lib.pa_decode_cascade_workspace_size.argtypes = [_I32] * 7
+    lib.pa_decode_cascade_workspace_size.restype = ctypes.c_size_t
+    lib.pa_decode_cascade.argtypes = ([_P] * 5 + [_I32] + [_P] * 2 + [_I32] * 6
+                                      + [ctypes.c_float, _I32, _P, ctypes.c_size_t, _P])
+    lib.pa_decode_cascade.restype = ctypes.c_int
+    lib.pa_multi_query.argtypes = [_P] * 7 + [_I32] * 8 + [ctypes.c_float, _P]
+    lib.pa_multi_query.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_swap_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, ctypes.c_int64, _P]
@@ -248,4 +255,73 @@ def decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_sc
                               _ptr(workspace), wbytes, _stream_ptr(stream))
     if rc != PA_OK:
         raise PAError(rc, "pa_decode_fp8")
+    return out
+
+
+def decode_cascade_workspace_size(num_seqs, num_heads, head_dim, block_size, prefix_len,
+                                  max_blocks_per_seq, partition_size):
+    return int(load().pa_decode_cascade_workspace_size(num_seqs, num_heads, head_dim, block_size,
+                                                       prefix_len, max_blocks_per_seq,
+                                                       partition_size))
+
+
+def decode_cascade(out, q, k_cache, v_cache, prefix_table, prefix_len, block_tables,
+                   context_lens, scale, partition_size=512, workspace=None, stream=None):
+    """Decode for sequences that all start with the same prefix: prefix_table
+    (int32 [prefix_len / B] GPU tensor) lists the prefix's blocks,
+    block_tables / context_lens the private suffixes.  Equals decode() over
+    prefix_table ++ block_tables[s] with context prefix_len + context_lens[s]."""
+    import torch
+    _check(k_cache, "k_cache", torch.float16, ndim=4)
+    NB, B, H, D = k_cache.shape
+    _check(v_cache, "v_cache", torch.float16, shape=k_cache.shape)
+    _check(q, "q", torch.float16, ndim=3)
+    S = q.shape[0]
+    _check(q, "q", torch.float16, shape=(S, H, D))
+    _check(out, "out", torch.float16, shape=(S, H, D))
+    _check(prefix_table, "prefix_table", torch.int32, ndim=1)
+    if prefix_len % B or prefix_table.numel() * B < prefix_len:
+        raise ValueError("prefix_len must be a multiple of the block size covered by prefix_table")
+    _check(block_tables, "block_tables", torch.int32, ndim=2)
+    MB = block_tables.shape[1]
+    _check(block_tables, "block_tables", torch.int32, shape=(S, MB))
+    _check(context_lens, "context_lens", torch.int32, shape=(S,))
+    need = decode_cascade_workspace_size(S, H, D, B, int(prefix_len), MB, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check(workspace, "workspace", torch.uint8, ndim=1)
+    rc = load().pa_decode_cascade(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(prefix_table), int(prefix_len), _ptr(block_tables),
+                                  _ptr(context_lens), S, H, D, NB, B, MB, float(scale),
+                                  int(partition_size), _ptr(workspace), workspace.numel(),
+                                  _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_decode_cascade")
+    return out
+
+
+def multi_query(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len,
+                scale, stream=None):
+    """Multi-query (chunked-prefill) paged attention: the rows
+    query_start[s] .. query_start[s+1]-1 of q [T, H, D] are the last positions
+    of sequence s and attend causally through its block table."""
+    import torch
+    _check(k_cache, "k_cache", torch.float16, ndim=4)
+    NB, B, H, D = k_cache.shape
+    _check(v_cache, "v_cache", torch.float16, shape=k_cache.shape)
+    _check(q, "q", torch.float16, ndim=3)
+    T = q.shape[0]
+    _check(q, "q", torch.float16, shape=(T, H, D))
+    _check(out, "out", torch.float16, shape=(T, H, D))
+    _check(block_tables, "block_tables", torch.int32, ndim=2)
+    S, MB = block_tables.shape
+    _check(context_lens, "context_lens", torch.int32, shape=(S,))
+    _check(query_start, "query_start", torch.int32, shape=(S + 1,))
+    rc = load().pa_multi_query(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_tables), _ptr(context_lens), _ptr(query_start), S, T,
+                               int(max_query_len), H, D, NB, B, MB, float(scale),
+                               _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_multi_query")
     return out

@@ -106,12 +106,15 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
 
 namespace {
 
-// Shared checks and parameter set-up of pa_decode and pa_decode_fp8.
+// Shared checks and parameter set-up of pa_decode, pa_decode_fp8 and the
+// suffix part of pa_decode_cascade (extra_slots = 1 there: slot 0 of every
+// (sequence, head) holds the shared-prefix partial).
 int prepare_decode(pa::DecodeParams& p, void* out, const void* q, const void* k_cache,
                    const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                    int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
                    int32_t block_size, int32_t max_blocks_per_seq, float scale,
-                   int32_t partition_size, void* workspace, size_t workspace_bytes)
+                   int32_t partition_size, void* workspace, size_t workspace_bytes,
+                   int32_t extra_slots = 0)
 {
     if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0 ||
         max_blocks_per_seq <= 0)
@@ -135,7 +138,8 @@ int prepare_decode(pa::DecodeParams& p, void* out, const void* q, const void* k_
 
     const int64_t np = num_partitions(block_size, max_blocks_per_seq, partition_size);
     const int64_t units = (int64_t)num_seqs * num_heads * np;
-    if (units > INT32_MAX || (int64_t)num_seqs * num_heads > INT32_MAX)
+    const int64_t slots = np + extra_slots;
+    if (units > INT32_MAX || (int64_t)num_seqs * num_heads * slots > INT32_MAX)
         return PA_ERR_INVALID_DIM;
 
     p = pa::DecodeParams{};
@@ -153,8 +157,10 @@ int prepare_decode(pa::DecodeParams& p, void* out, const void* q, const void* k_
     p.total_units = (uint32_t)units;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);  // log2(e)
     p.v_scale = 1.0f;
-    if (np > 1) {
-        const WorkspaceLayout w = layout(units, head_dim);
+    p.slot_base = extra_slots;
+    p.num_slots = (int32_t)slots;
+    if (slots > 1) {
+        const WorkspaceLayout w = layout((int64_t)num_seqs * num_heads * slots, head_dim);
         if (!workspace || workspace_bytes < w.total)
             return PA_ERR_WORKSPACE;
         if (!aligned16(workspace))
@@ -170,6 +176,121 @@ int prepare_decode(pa::DecodeParams& p, void* out, const void* q, const void* k_
 bool valid_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
 }  // namespace
+
+namespace {
+constexpr int32_t kPrefixPartLen = 64;  // shared-prefix tokens per matrix-core wave
+
+int32_t prefix_parts(int32_t prefix_len) { return (prefix_len + kPrefixPartLen - 1) / kPrefixPartLen; }
+}  // namespace
+
+size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t prefix_len,
+                                        int32_t max_blocks_per_seq, int32_t partition_size)
+{
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || prefix_len < 0 ||
+        max_blocks_per_seq <= 0 || partition_size < 0 || partition_size % block_size != 0)
+        return 0;
+    if (prefix_len == 0)
+        return pa_decode_workspace_size(num_seqs, num_heads, head_dim, block_size,
+                                        max_blocks_per_seq, partition_size);
+    const int64_t slots =
+        prefix_parts(prefix_len) + num_partitions(block_size, max_blocks_per_seq, partition_size);
+    return layout((int64_t)num_seqs * num_heads * slots, head_dim).total;
+}
+
+int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* prefix_block_table, int32_t prefix_len,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                      int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (prefix_len < 0 || (block_size > 0 && prefix_len % block_size != 0))
+        return PA_ERR_INVALID_DIM;
+    if (prefix_len == 0)  // nothing shared: the plain decode
+        return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                         num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq, scale,
+                         partition_size, workspace, workspace_bytes, stream);
+    if (head_dim != 64 && head_dim != 128)
+        return PA_ERR_UNSUPPORTED;
+    pa::DecodeParams p;
+    const int32_t parts = prefix_parts(prefix_len);
+    int rc = prepare_decode(p, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                            num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq, scale,
+                            partition_size, workspace, workspace_bytes, /*extra_slots=*/parts);
+    if (rc != PA_OK)
+        return rc == 1 ? PA_OK : rc;
+    if (!prefix_block_table)
+        return PA_ERR_NULL;
+    if (((int64_t)num_seqs + 15) / 16 * num_heads * parts > INT32_MAX)
+        return PA_ERR_INVALID_DIM;
+    pa::MqParams m{};
+    m.ws_o = p.ws_o;
+    m.ws_m = p.ws_m;
+    m.ws_l = p.ws_l;
+    m.q = static_cast<const _Float16*>(q);
+    m.k_cache = static_cast<const _Float16*>(k_cache);
+    m.v_cache = static_cast<const _Float16*>(v_cache);
+    m.prefix_table = prefix_block_table;
+    m.num_seqs = num_seqs;
+    m.num_heads = num_heads;
+    m.prefix_len = prefix_len;
+    m.prefix_part_len = kPrefixPartLen;
+    m.prefix_parts = parts;
+    m.num_slots = p.num_slots;
+    m.total_units = (uint32_t)(((int64_t)num_seqs + 15) / 16 * parts * num_heads);
+    m.scale_log2 = p.scale_log2;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = pa::launch_cascade_prefix(m, head_dim, block_size, st);
+    if (e == hipSuccess)
+        e = pa::launch_decode_dispatch(p, head_dim, block_size, st);
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                   int32_t max_query_len, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                   int32_t block_size, int32_t max_blocks_per_seq, float scale, void* stream)
+{
+    if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_heads <= 0 || head_dim <= 0 ||
+        num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0)
+        return PA_ERR_INVALID_DIM;
+    if (!supported_decode(head_dim, block_size))
+        return PA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale) || (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+        return PA_ERR_INVALID_DIM;
+    if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0)
+        return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+        return PA_ERR_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+        (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(query_start) & 3u))
+        return PA_ERR_ALIGN;
+    const int64_t chunks = ((int64_t)max_query_len + 15) / 16;
+    const int64_t units = (int64_t)num_seqs * chunks * num_heads;
+    if (units > INT32_MAX)
+        return PA_ERR_INVALID_DIM;
+    pa::MqParams m{};
+    m.out = static_cast<_Float16*>(out);
+    m.q = static_cast<const _Float16*>(q);
+    m.k_cache = static_cast<const _Float16*>(k_cache);
+    m.v_cache = static_cast<const _Float16*>(v_cache);
+    m.block_tables = block_tables;
+    m.context_lens = context_lens;
+    m.query_start = query_start;
+    m.num_seqs = num_seqs;
+    m.num_heads = num_heads;
+    m.max_blocks_per_seq = max_blocks_per_seq;
+    m.max_chunks = (int32_t)chunks;
+    m.total_units = (uint32_t)units;
+    m.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    hipError_t e = pa::launch_multiquery(m, head_dim, block_size,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,

@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
     const int64_t row = ((int64_t)s * P.num_heads + h) * D;
 
     if (ctx <= 0) {  // empty context: zero row, written by partition 0 only
-        if (part == 0 && threadIdx.x < D)
+        if (part == 0 && threadIdx.x < D && P.slot_base == 0)
             P.out[row + threadIdx.x] = (_Float16)0.0f;
         return;
     }
@@ -374,10 +374,10 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
         o = o / L;
         if constexpr (KV::kScaledOutput)
             o *= P.v_scale;
-        if (nparts_seq == 1) {
+        if (nparts_seq == 1 && P.slot_base == 0) {
             P.out[row + d] = (_Float16)o;
         } else {
-            const int64_t u = ((int64_t)s * P.num_heads + h) * P.num_partitions + part;
+            const int64_t u = ((int64_t)s * P.num_heads + h) * P.num_slots + P.slot_base + part;
             P.ws_o[u * D + d] = o;
             if (d == 0) {
                 P.ws_m[u] = M;
@@ -400,15 +400,16 @@ __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
     const int sh = blockIdx.x;
     const int s = sh / P.num_heads;
     const int ctx = P.context_lens[s];
-    const int np = (ctx + P.partition_size - 1) / P.partition_size;
-    if (np <= 1)
-        return;
+    // slots in use: the shared-prefix slot (if any) + this sequence's partitions
+    const int np = P.slot_base + (ctx + P.partition_size - 1) / P.partition_size;
+    if (np == 0 || (np == 1 && P.slot_base == 0))
+        return;  // nothing to merge (an unsplit sequence wrote its own row)
     const int t = threadIdx.x;
     const int lane = t % kWave;
     const int wave = t / kWave;
     const int g = t / D;
     const int d = t % D;
-    const int64_t u0 = (int64_t)sh * P.num_partitions;
+    const int64_t u0 = (int64_t)sh * P.num_slots;
     const float* m = P.ws_m + u0;
     const float* l = P.ws_l + u0;
     const float* o = P.ws_o + u0 * D;
@@ -464,7 +465,7 @@ hipError_t launch_decode(const DecodeParams& P, hipStream_t stream)
 {
     hipLaunchKernelGGL((pa_partition_kernel<KV, D, B>), dim3(P.total_units), dim3(kThreads), 0,
                        stream, P);
-    if (P.num_partitions > 1)
+    if (P.num_slots > 1)
         hipLaunchKernelGGL((pa_reduce_kernel<D>), dim3(P.num_seqs * P.num_heads), dim3(kThreads),
                            0, stream, P);
     return hipGetLastError();

@@ -25,7 +25,39 @@ struct DecodeParams {
     uint32_t total_units;    // num_seqs * num_heads * num_partitions workgroups
     float scale_log2;        // scale * log2(e) (times the K scale for FP8)
     float v_scale;           // FP8: dequantisation scale of V (unused for fp16)
+    int32_t slot_base;       // first workspace slot of partition 0 (1 when a shared-prefix
+                             // partial occupies slot 0; partials are then always written)
+    int32_t num_slots;       // workspace slots per (sequence, head) = slot_base + num_partitions
 };
+
+// Several query rows against one K/V token stream (multi-query / shared prefix).
+struct MqParams {
+    _Float16* out;                 // multi-query: final rows [T, H, D]
+    float* ws_o;                   // shared prefix: partials, slot 0 of each (s, h)
+    float* ws_m;
+    float* ws_l;
+    const _Float16* q;             // multi-query: [T, H, D]; shared prefix: [S, H, D]
+    const _Float16* k_cache;
+    const _Float16* v_cache;
+    const int32_t* block_tables;   // multi-query: [S, MB]
+    const int32_t* context_lens;   // multi-query: [S] (including the new tokens)
+    const int32_t* query_start;    // multi-query: [S + 1]
+    const int32_t* prefix_table;   // shared prefix: the prefix's physical blocks
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t max_blocks_per_seq;
+    int32_t max_chunks;            // multi-query: ceil(max query rows / 16)
+    int32_t prefix_len;            // shared prefix: tokens in the prefix
+    int32_t prefix_part_len;       // shared prefix: tokens per prefix partition (multiple of 16)
+    int32_t prefix_parts;          // shared prefix: partitions = workspace slots 0..parts-1
+    int32_t num_slots;             // shared prefix: workspace slots per (s, h)
+    uint32_t total_units;
+    float scale_log2;
+};
+
+hipError_t launch_multiquery(const MqParams& p, int head_dim, int block_size, hipStream_t stream);
+hipError_t launch_cascade_prefix(const MqParams& p, int head_dim, int block_size,
+                                 hipStream_t stream);
 
 hipError_t launch_decode_dispatch(const DecodeParams& p, int head_dim, int block_size,
                                   hipStream_t stream);

@@ -372,3 +372,31 @@ def fp8_pools(w, headroom=1.0):
     vs = scale_of(w.v_cache, w.value)
     return Fp8Pools(k_cache=quant(w.k_cache, ks), v_cache=quant(w.v_cache, vs), k_scale=ks,
                     v_scale=vs)
+
+
+def make_multi_query(context_lens, query_lens, num_heads, head_dim, block_size, seed=0,
+                     poison=True):
+    """Inputs of a multi-query (chunked prefill / mixed) batch: sequence s has
+    context_lens[s] positions in the cache, of which the last query_lens[s]
+    are this step's new tokens; q holds their rows, query_start the offsets.
+    Returns (Workload, q [T, H, D] fp16, query_start [S + 1] int32)."""
+    w = make_random(context_lens, num_heads, head_dim, block_size, seed=seed, poison=poison)
+    qlen = np.asarray(query_lens, dtype=np.int64)
+    assert np.all(qlen <= w.context_lens) and np.all(qlen >= 0)
+    qs = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    ss = np.random.SeedSequence([SEED, 2000, seed])
+    q = _normal_f16(ss, (int(qs[-1]), w.num_heads, w.head_dim))
+    return w, q, qs
+
+
+def split_shared_prefix(w, prefix_blocks):
+    """For a workload whose tables all start with the same prefix_blocks ids
+    (the shared-prefix configuration): the prefix table, its length, and the
+    suffix tables / lengths that pa_decode_cascade takes."""
+    prefix = w.block_tables[0, :prefix_blocks].copy()
+    assert np.all(w.block_tables[:, :prefix_blocks] == prefix)
+    B = w.block_size
+    suffix_tables = np.ascontiguousarray(w.block_tables[:, prefix_blocks:])
+    suffix_lens = (w.context_lens - prefix_blocks * B).astype(np.int32)
+    assert np.all(suffix_lens >= 0)
+    return prefix.astype(np.int32), prefix_blocks * B, suffix_tables, suffix_lens
