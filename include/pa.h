@@ -142,9 +142,10 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * ([eng] §3.2, [10x] §4.4: several tables list the same physical blocks).
  * The result equals pa_decode over the tables prefix_block_table ++
  * block_tables[s] with context prefix_len + context_lens[s]; it is computed
- * so that the prefix is read once per 16 sequences and head (matrix-core
- * passes of 16 queries against 64-token pieces of the prefix) and each
- * suffix once, all pieces merged with the log-sum-exp identity.
+ * so that the prefix is read once per 64 sequences and head (a workgroup
+ * stages 64-token pieces of the prefix in LDS for the matrix-core products of
+ * 64 queries) and each suffix once, all pieces merged with the log-sum-exp
+ * identity.
  *
  *   prefix_block_table  int32 [prefix_len / block_size], DEVICE: the prefix's
  *                       physical blocks in logical order
@@ -154,7 +155,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  *   context_lens        the private suffixes: [num_seqs, max_blocks_per_seq]
  *                       and [num_seqs] (suffix lengths, 0 allowed)
  *   workspace           at least pa_decode_cascade_workspace_size(...) bytes
- * Other arguments, layouts and errors as pa_decode.  head_dim 64 or 128,
+ * Other arguments, layouts and errors as pa_decode, except that scale must
+ * be finite and > 0 (else PA_ERR_INVALID_DIM).  head_dim 64 or 128,
  * block_size 16 or 32.
  */
 size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
@@ -185,7 +187,10 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
  *                  query_start[0] = 0, query_start[num_seqs] = num_tokens
  *   max_query_len  an upper bound of every n_s (sizes the launch)
  *   block_tables, context_lens  as pa_decode; n_s <= context_lens[s]
- * head_dim 64 or 128, block_size 16 or 32.  No workspace.
+ *   scale          finite and > 0 (else PA_ERR_INVALID_DIM)
+ * head_dim 64 or 128, block_size 16 or 32.  No workspace.  Rows are
+ * processed in tiles of 64 per (sequence, head); a K/V chunk of 64 tokens is
+ * read once per tile.
  */
 int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* block_tables, const int32_t* context_lens,

@@ -178,7 +178,7 @@ bool valid_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 }  // namespace
 
 namespace {
-constexpr int32_t kPrefixPartLen = 64;  // shared-prefix tokens per matrix-core wave
+constexpr int32_t kPrefixPartLen = pa::kMqChunk;  // shared-prefix tokens per workgroup
 
 int32_t prefix_parts(int32_t prefix_len) { return (prefix_len + kPrefixPartLen - 1) / kPrefixPartLen; }
 }  // namespace
@@ -207,6 +207,8 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
 {
     if (prefix_len < 0 || (block_size > 0 && prefix_len % block_size != 0))
         return PA_ERR_INVALID_DIM;
+    if (!(std::isfinite(scale) && scale > 0.0f))
+        return PA_ERR_INVALID_DIM;
     if (prefix_len == 0)  // nothing shared: the plain decode
         return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                          num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq, scale,
@@ -222,7 +224,8 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
         return rc == 1 ? PA_OK : rc;
     if (!prefix_block_table)
         return PA_ERR_NULL;
-    if (((int64_t)num_seqs + 15) / 16 * num_heads * parts > INT32_MAX)
+    const int64_t row_tiles = ((int64_t)num_seqs + pa::kCascadeTileRows - 1) / pa::kCascadeTileRows;
+    if (row_tiles * num_heads * parts > INT32_MAX)
         return PA_ERR_INVALID_DIM;
     pa::MqParams m{};
     m.ws_o = p.ws_o;
@@ -238,7 +241,8 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
     m.prefix_part_len = kPrefixPartLen;
     m.prefix_parts = parts;
     m.num_slots = p.num_slots;
-    m.total_units = (uint32_t)(((int64_t)num_seqs + 15) / 16 * parts * num_heads);
+    m.row_tiles = (int32_t)row_tiles;
+    m.total_units = (uint32_t)(row_tiles * parts * num_heads);
     m.scale_log2 = p.scale_log2;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = pa::launch_cascade_prefix(m, head_dim, block_size, st);
@@ -258,7 +262,8 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
         return PA_ERR_INVALID_DIM;
     if (!supported_decode(head_dim, block_size))
         return PA_ERR_UNSUPPORTED;
-    if (!std::isfinite(scale) || (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    if (!(std::isfinite(scale) && scale > 0.0f) ||
+        (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
         return PA_ERR_INVALID_DIM;
     if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0)
         return PA_OK;
@@ -269,8 +274,8 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
         (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
         (reinterpret_cast<uintptr_t>(query_start) & 3u))
         return PA_ERR_ALIGN;
-    const int64_t chunks = ((int64_t)max_query_len + 15) / 16;
-    const int64_t units = (int64_t)num_seqs * chunks * num_heads;
+    const int64_t tiles = ((int64_t)max_query_len + pa::kMqTileRows - 1) / pa::kMqTileRows;
+    const int64_t units = (int64_t)num_seqs * tiles * num_heads;
     if (units > INT32_MAX)
         return PA_ERR_INVALID_DIM;
     pa::MqParams m{};
@@ -284,7 +289,7 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
     m.num_seqs = num_seqs;
     m.num_heads = num_heads;
     m.max_blocks_per_seq = max_blocks_per_seq;
-    m.max_chunks = (int32_t)chunks;
+    m.row_tiles = (int32_t)tiles;
     m.total_units = (uint32_t)units;
     m.scale_log2 = (float)((double)scale * 1.4426950408889634074);
     hipError_t e = pa::launch_multiquery(m, head_dim, block_size,

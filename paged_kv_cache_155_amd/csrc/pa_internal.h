@@ -31,6 +31,11 @@ struct DecodeParams {
 };
 
 // Several query rows against one K/V token stream (multi-query / shared prefix).
+constexpr int kMqThreads = 256;       // threads per workgroup (4 waves)
+constexpr int kMqChunk = 64;          // tokens staged in LDS per step
+constexpr int kMqTileRows = 64;       // multi-query rows per workgroup
+constexpr int kCascadeTileRows = 64;  // shared-prefix sequences per workgroup
+
 struct MqParams {
     _Float16* out;                 // multi-query: final rows [T, H, D]
     float* ws_o;                   // shared prefix: partials, slot 0 of each (s, h)
@@ -46,9 +51,11 @@ struct MqParams {
     int32_t num_seqs;
     int32_t num_heads;
     int32_t max_blocks_per_seq;
-    int32_t max_chunks;            // multi-query: ceil(max query rows / 16)
+    int32_t row_tiles;             // tiles of query rows per stream: multi-query
+                                   // ceil(max query rows / kMqTileRows), shared prefix
+                                   // ceil(num_seqs / kCascadeTileRows)
     int32_t prefix_len;            // shared prefix: tokens in the prefix
-    int32_t prefix_part_len;       // shared prefix: tokens per prefix partition (multiple of 16)
+    int32_t prefix_part_len;       // shared prefix: tokens per prefix partition (multiple of kMqChunk)
     int32_t prefix_parts;          // shared prefix: partitions = workspace slots 0..parts-1
     int32_t num_slots;             // shared prefix: workspace slots per (s, h)
     uint32_t total_units;

@@ -8,36 +8,39 @@
 //   [eng]  "深入解析LLM推理引擎：从PagedAttention到调度优化" §3.2 (shared
 //          prefix blocks), §4.2 (mixed prefill / decode batches)
 //
-// Two uses of one kernel, each a group of up to 16 query rows per wave:
-//   * multi-query (chunked prefill): 16 consecutive new tokens of one
-//     sequence; row r at logical position p_r sees positions 0..p_r;
-//   * shared prefix (cascade decode): the decode queries of 16 sequences that
-//     all list the same prefix blocks first; every row sees the whole prefix,
-//     which is therefore read once per 16 sequences instead of once per
-//     sequence.  The prefix is cut into partitions of a few blocks (one wave
-//     each, so the short stream still fills the chip); each yields a
-//     log-sum-exp partial that the decode reduce merges with the partials of
-//     the private suffixes.
+// Two uses of one kernel; a workgroup of 4 waves owns a tile of query rows
+// (16 * QT per wave) that all read the same token stream:
+//   * multi-query (chunked prefill): consecutive new tokens of one sequence;
+//     row r at logical position p_r sees positions 0..p_r;
+//   * shared prefix (cascade decode): the decode queries of many sequences
+//     that all list the same prefix blocks first; every row sees the whole
+//     prefix, which is therefore read once per tile of sequences instead of
+//     once per sequence.  The prefix is cut into partitions so that the short
+//     stream still fills the chip; each yields a log-sum-exp partial that the
+//     decode reduce merges with the partials of the private suffixes.
 //
-// Per 16-token block of the stream (always inside one physical block, B is
-// 16 or 32), with K, V rows of one head loaded as 16-byte vectors:
-//   S^T = K Q^T   8 x v_mfma_f32_16x16x16f16 (k runs over the head dim; each
-//                 lane group of 16 lanes owns a contiguous quarter of the
-//                 dims, so K and Q are read as they lie in memory)
-//   online softmax per query row on the S^T tile (lane = query, 4 tokens
-//                 per lane), base-2 exponent
-//   O^T += V^T P^T  8 x v_mfma_f32_16x16x16f16: the S^T tile is already P^T
-//                 in the B-operand layout, and O^T comes out with the query
-//                 as the lane's column, like the softmax state, so rescaling
-//                 needs no cross-lane traffic.  V goes through LDS in its own
-//                 row layout (16-byte stores, rows padded to 136 halves so the
-//                 four lane groups use different banks); each lane then reads
-//                 its 4 tokens of one column as 2-byte values.
-// The K/V loads of the next block are issued before the current block is
-// computed (register double buffering), so one block's latency hides behind
-// the previous block's math.
-// Positions past the stream end get -inf scores and zero V rows (select, not
-// multiply), so unread slots may hold anything.
+// Per 64-token chunk of the stream:
+//   * the 256 threads load it once (each: 4 consecutive tokens x 8 dims of
+//     K and of V, 16-byte loads through the block table) and stage it in LDS,
+//     double buffered so one barrier per chunk suffices; K keeps its row
+//     layout, V is transposed on the way in (4 x 8 halves per thread, 8-byte
+//     stores into rows of 72 halves with the 4-token group XOR-swizzled by
+//     dim / 8, which keeps both the stores and the MFMA-operand reads free of
+//     bank conflicts); the next chunk's loads are issued before the math;
+//   * each wave, for its 16 * QT rows:
+//       S^T = K Q^T      v_mfma_f32_16x16x32_f16 over the head dim (each lane
+//                        group owns a contiguous quarter of the dims, so K and
+//                        Q are read as they lie)
+//       online softmax   per query column (lane = query, 16 tokens per lane),
+//                        base-2 exponent; the running max is exchanged across
+//                        the four lane groups with permlane swaps, the running
+//                        sum stays per lane until the end; O is rescaled only
+//                        when some row's max moved
+//       O^T += V^T P^T   v_mfma_f32_16x16x32_f16 over 32 tokens; the S^T
+//                        tiles are already P^T in the B-operand layout
+// Positions past a row's limit get -inf scores; K/V rows past the stream end
+// are loaded as zeros (select, not multiply), so unread slots may hold
+// anything.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,17 +50,33 @@ namespace pa {
 namespace {
 
 constexpr int kWave = 64;
+constexpr int kWaves = kMqThreads / kWave;
 constexpr float kNegInf = -__builtin_inff();
 
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ h4 lo_h4(const u32x4& v) { return __builtin_bit_cast(h4, u32x2{v.x, v.y}); }
-__device__ __forceinline__ h4 hi_h4(const u32x4& v) { return __builtin_bit_cast(h4, u32x2{v.z, v.w}); }
+__device__ __forceinline__ h8 as_h8(const u32x4& v) { return __builtin_bit_cast(h8, v); }
+
+// max / sum over the four 16-lane groups (lanes c, c+16, c+32, c+48)
+__device__ __forceinline__ float group_max(float x)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float x)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // Hardware workgroup i of n lands on XCD i % 8; XCD x gets logical range
 // [x*n/8, (x+1)*n/8).
@@ -69,185 +88,248 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n)
     return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
 
-template <int D, int B, bool kCascade>
-__global__ __launch_bounds__(kWave) void pa_mq_kernel(MqParams P)
+template <int D, int B, bool kCascade, int QT>
+__global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
 {
-    constexpr int NB = D / 16;     // 16-column blocks of the output
-    constexpr int LPR = D / 32;    // 16-byte loads per lane per K (or V) row quarter
-    constexpr int VS = D + 8;      // LDS row stride (halves) of the V tile
-    static_assert(B % 16 == 0, "16-token blocks must stay inside one physical block");
+    constexpr int N = kMqChunk;           // tokens per staged chunk
+    constexpr int NB = D / 16;            // 16-dim blocks of O^T
+    constexpr int KI = D / 32;            // MFMA k-steps over the head dim
+    constexpr int KS = D + 8;             // LDS row stride (halves) of the K tile
+    constexpr int VTS = N + 8;            // LDS row stride (halves) of the V^T tile
+    constexpr int WROWS = 16 * QT;        // query rows per wave
+    constexpr int ROWS = kWaves * WROWS;  // query rows per workgroup
+    constexpr int DG = D / 8;             // 8-dim groups per token row
+    constexpr int UNITS = (N / 4) * DG;   // 4-token x 8-dim load units per chunk
+    static_assert(N == 64 && UNITS <= kMqThreads && DG <= 16, "chunk geometry");
+    static_assert(B % 4 == 0, "a 4-token load unit must stay inside one physical block");
+    static_assert(ROWS == (kCascade ? kCascadeTileRows : kMqTileRows), "tile rows");
 
-    const int lane = threadIdx.x;
-    const int g = lane / 16;       // lane group: owns dims [g*D/4, (g+1)*D/4)
-    const int c = lane % 16;       // this lane's query column of S^T (and token row of K)
+    __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][N * KS];  // [token][dim]
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][D * VTS]; // [dim][token (swizzled)]
 
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int g = lane / 16;  // lane group: owns dims [g*D/4, (g+1)*D/4) of K and Q
+    const int c = lane % 16;  // this lane's query column of S^T (and token row of K)
+
+    // ---- the tile of query rows and the token stream they share ----
     const uint32_t logical = xcd_remap(blockIdx.x, P.total_units);
-    const int h = (int)(logical % (uint32_t)P.num_heads);
-    const int unit = (int)(logical / (uint32_t)P.num_heads);
-
-    // ---- the 16 query rows of this unit and the token stream they share ----
-    int s_first = 0, seq = 0, n_rows = 0, limit = 0, stream_begin = 0, stream_end = 0;
-    int part = 0;
-    int64_t q_row = 0;
+    const int tile = (int)(logical % (uint32_t)P.row_tiles);
+    const uint32_t rest = logical / (uint32_t)P.row_tiles;
+    int h, n_rows, stream_begin = 0, stream_end, lim0 = 0, part = 0;
+    int64_t row0;  // q row (multi-query) or sequence (shared prefix) of tile row 0
     const int32_t* table;
     if constexpr (kCascade) {
-        part = unit % P.prefix_parts;            // prefix tokens [part*len, (part+1)*len)
-        s_first = (unit / P.prefix_parts) * 16;  // sequences s_first .. s_first+15
-        n_rows = min(16, P.num_seqs - s_first);
-        seq = s_first + c;
-        q_row = seq;
+        part = (int)(rest % (uint32_t)P.prefix_parts);  // prefix tokens [part*len, (part+1)*len)
+        h = (int)(rest / (uint32_t)P.prefix_parts);
+        row0 = (int64_t)tile * ROWS;
+        n_rows = min(ROWS, P.num_seqs - (int)row0);
         stream_begin = part * P.prefix_part_len;
         stream_end = min(stream_begin + P.prefix_part_len, P.prefix_len);
-        limit = c < n_rows ? stream_end : 0;
         table = P.prefix_table;
     } else {
-        const int chunk = unit % P.max_chunks;   // 16-row chunk of a sequence's new tokens
-        seq = unit / P.max_chunks;
+        h = (int)(rest % (uint32_t)P.num_heads);
+        const int seq = (int)(rest / (uint32_t)P.num_heads);
         const int q0 = P.query_start[seq];
         const int n = P.query_start[seq + 1] - q0;
-        const int r0 = chunk * 16;
+        const int r0 = tile * ROWS;
         if (r0 >= n)
-            return;
-        n_rows = min(16, n - r0);
-        const int ctx = P.context_lens[seq];
-        q_row = q0 + r0 + c;
-        limit = c < n_rows ? ctx - n + r0 + c + 1 : 0;
-        stream_end = ctx - n + r0 + n_rows;      // the last row's position + 1
+            return;  // the whole workgroup, before any barrier
+        n_rows = min(ROWS, n - r0);
+        row0 = q0 + r0;
+        lim0 = P.context_lens[seq] - n + r0 + 1;  // tile row r sees positions < lim0 + r
+        stream_end = lim0 + n_rows - 1;
         table = P.block_tables + (int64_t)seq * P.max_blocks_per_seq;
     }
 
-    // Q^T as MFMA B operand: lane (query c) holds dims [g*D/4, g*D/4 + D/4).
-    u32x4 qf[LPR];
-    {
-        const bool valid = c < n_rows;
-        const u32x4* qp = reinterpret_cast<const u32x4*>(
-            P.q + (q_row * P.num_heads + h) * D + g * (D / 4));
+    // rows of this wave, their visibility limits (wave-uniform bounds)
+    const int wr0 = wave * WROWS;
+    const int wrows = max(0, min(WROWS, n_rows - wr0));
+    const int wave_lo = kCascade ? stream_end : lim0 + wr0;              // smallest limit
+    const int wave_hi = kCascade ? stream_end : lim0 + wr0 + wrows - 1;  // largest limit
+    int lim[QT];
 #pragma unroll
-        for (int i = 0; i < LPR; ++i)
-            qf[i] = valid ? qp[i] : u32x4{0, 0, 0, 0};
+    for (int qt = 0; qt < QT; ++qt)
+        lim[qt] = kCascade ? stream_end : lim0 + wr0 + 16 * qt + c;
+
+    // Q^T as MFMA B operand: lane (query c) holds dims g*D/4 + 8i .. +7 for step i
+    u32x4 qf[QT][KI];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int r = wr0 + 16 * qt + c;
+        const u32x4* qp =
+            reinterpret_cast<const u32x4*>(P.q + ((row0 + r) * P.num_heads + h) * D + g * (D / 4));
+#pragma unroll
+        for (int i = 0; i < KI; ++i)
+            qf[qt][i] = r < n_rows ? qp[i] : u32x4{0, 0, 0, 0};
     }
 
-    f4 o[NB];
+    f4 o[QT][NB];
+    float m[QT], lpart[QT];  // running max (scaled, base 2) and this lane's share of the sum
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        o[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m = kNegInf, lsum = 0.0f;  // softmax state of query c
-
-    __shared__ __attribute__((aligned(16))) _Float16 vt[16 * VS];  // V of one block: [token][dim]
-
-    const int64_t block_elems = (int64_t)B * P.num_heads * D;
-    const int token_stride = P.num_heads * D;
-    const int lane_elem = h * D + g * (D / 4);
-    // K/V of the 16-token block at t (this lane: token t + c, its quarter of the dims)
-    auto load_block = [&](int t, u32x4* kd, u32x4* vd) {
-        const int pb = table[t / B];
-        const int64_t e = (int64_t)pb * block_elems + (int64_t)((t % B) + c) * token_stride +
-                          lane_elem;
-#pragma unroll
-        for (int i = 0; i < LPR; ++i) {
-            kd[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(P.k_cache + e) + i);
-            vd[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(P.v_cache + e) + i);
-        }
-    };
-    u32x4 kr[LPR], vr[LPR];
-    if (stream_begin < stream_end)
-        load_block(stream_begin, kr, vr);
-    for (int t0 = stream_begin; t0 < stream_end; t0 += 16) {
-        const bool live = t0 + c < stream_end;   // this lane's K/V token exists
-        u32x4 kn[LPR], vn[LPR];
-        if (t0 + 16 < stream_end)
-            load_block(t0 + 16, kn, vn);
-
-        // S^T[token 4g+j][query c] over the head dim
-        f4 st = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < LPR; ++i) {
-            st = __builtin_amdgcn_mfma_f32_16x16x16f16(lo_h4(kr[i]), lo_h4(qf[i]), st, 0, 0, 0);
-            st = __builtin_amdgcn_mfma_f32_16x16x16f16(hi_h4(kr[i]), hi_h4(qf[i]), st, 0, 0, 0);
-        }
-
-        // online softmax for query c over tokens t0 + 4g + j
-        float x[4];
-        float bmax = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool vis = t0 + 4 * g + j < limit;
-            x[j] = vis ? st[j] * P.scale_log2 : kNegInf;
-            bmax = fmaxf(bmax, x[j]);
-        }
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-        const float m_new = fmaxf(m, bmax);
-        const float m_ref = m_new == kNegInf ? 0.0f : m_new;
-        const float alpha = exp2_fast(m - m_ref);
-        h4 pa;
-        float psum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float p = exp2_fast(x[j] - m_ref);
-            psum += p;
-            pa[j] = (_Float16)p;
-        }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-        lsum = lsum * alpha + psum;
-        m = m_new;
-
-        // rescale this query's columns of O^T
+    for (int qt = 0; qt < QT; ++qt) {
+        m[qt] = kNegInf;
+        lpart[qt] = 0.0f;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[nb][j] *= alpha;
+            o[qt][nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
-        // V block -> LDS as it lies in memory (rows past the stream end are zero)
-        {
-            u32x4* row = reinterpret_cast<u32x4*>(&vt[c * VS + g * (D / 4)]);
+    // ---- loader role: 4 tokens (4*lq .. 4*lq+3 of the chunk) x dims 8*lp .. 8*lp+7 ----
+    const bool loader = tid < UNITS;
+    const int lp = tid % DG, lq = tid / DG;
+    const int64_t block_elems = (int64_t)B * P.num_heads * D;
+    const int token_stride = P.num_heads * D;
+    u32x4 kr[4], vr[4];
+    auto load_chunk = [&](int t0) {
+        const int t = t0 + 4 * lq;
+        const bool any = loader && t < stream_end;
+        const int64_t base = any ? (int64_t)table[t / B] * block_elems +
+                                       (int64_t)(t % B) * token_stride + h * D + 8 * lp
+                                 : 0;
 #pragma unroll
-            for (int i = 0; i < LPR; ++i)
-                row[i] = live ? vr[i] : u32x4{0, 0, 0, 0};
+        for (int j = 0; j < 4; ++j) {
+            const bool ok = any && t + j < stream_end;
+            const int64_t e = base + (int64_t)j * token_stride;
+            kr[j] = ok ? *reinterpret_cast<const u32x4*>(P.k_cache + e) : u32x4{0, 0, 0, 0};
+            vr[j] = ok ? *reinterpret_cast<const u32x4*>(P.v_cache + e) : u32x4{0, 0, 0, 0};
         }
-        __syncthreads();
-        // A operand V^T[column 16nb + c][token 4g + j]
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            h4 va;
+    };
+
+    load_chunk(stream_begin);
+    int buf = 0;
+    for (int t0 = stream_begin; t0 < stream_end; t0 += N, buf ^= 1) {
+        _Float16* ks = k_lds[buf];
+        _Float16* vs = v_lds[buf];
+        if (loader) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                va[j] = vt[(4 * g + j) * VS + nb * 16 + c];
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pa, o[nb], 0, 0, 0);
-        }
-        __syncthreads();  // the tile is rewritten next iteration
+                *reinterpret_cast<u32x4*>(&ks[(4 * lq + j) * KS + 8 * lp]) = kr[j];
+            // V^T: dim 8lp+e, tokens 4lq..4lq+3 -> one 8-byte store per dim
+            const int col = 4 * (lq ^ lp);  // swizzle (dim / 8) % 16 == lp
 #pragma unroll
-        for (int i = 0; i < LPR; ++i) {
-            kr[i] = kn[i];
-            vr[i] = vn[i];
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t a = vr[0][w], b = vr[1][w], cc = vr[2][w], d = vr[3][w];
+                const u32x2 even{(a & 0xffffu) | (b << 16), (cc & 0xffffu) | (d << 16)};
+                const u32x2 odd{(a >> 16) | (b & 0xffff0000u), (cc >> 16) | (d & 0xffff0000u)};
+                *reinterpret_cast<u32x2*>(&vs[(8 * lp + 2 * w) * VTS + col]) = even;
+                *reinterpret_cast<u32x2*>(&vs[(8 * lp + 2 * w + 1) * VTS + col]) = odd;
+            }
+        }
+        if (t0 + N < stream_end)
+            load_chunk(t0 + N);  // in flight during this chunk's math
+        __syncthreads();
+
+        if (wrows > 0 && t0 < wave_hi) {  // wave-uniform: some row of this wave sees the chunk
+            // S^T[token 16s + 4g + j][query c] for the four 16-token subtiles
+            f4 st[QT][4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                u32x4 ka[KI];
+#pragma unroll
+                for (int i = 0; i < KI; ++i)
+                    ka[i] = *reinterpret_cast<const u32x4*>(&ks[(16 * s + c) * KS + g * (D / 4) + 8 * i]);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) {
+                    f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int i = 0; i < KI; ++i)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(ka[i]), as_h8(qf[qt][i]),
+                                                                     acc, 0, 0, 0);
+                    st[qt][s] = acc;
+                }
+            }
+
+            // online softmax per query column; P^T as the B operand of the next product
+            const bool need_mask = t0 + N > wave_lo;
+            h8 pb[QT][2];
+            bool moved = false;
+            float alpha[QT];
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                float bmax = kNegInf;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (need_mask && t0 + 16 * s + 4 * g + j >= lim[qt])
+                            st[qt][s][j] = kNegInf;
+                        bmax = fmaxf(bmax, st[qt][s][j]);
+                    }
+                // scale > 0, so the max of the raw scores gives the max of the scaled ones
+                const float m_new = fmaxf(m[qt], group_max(bmax) * P.scale_log2);
+                const float m_ref = m_new == kNegInf ? 0.0f : m_new;
+                alpha[qt] = exp2_fast(m[qt] - m_ref);
+                moved |= m_new != m[qt];
+                m[qt] = m_new;
+                float psum = 0.0f;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float p = exp2_fast(__builtin_fmaf(st[qt][s][j], P.scale_log2, -m_ref));
+                        psum += p;
+                        pb[qt][s / 2][4 * (s % 2) + j] = (_Float16)p;
+                    }
+                lpart[qt] = lpart[qt] * alpha[qt] + psum;
+            }
+            if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        o[qt][nb] *= alpha[qt];
+            }
+
+            // O^T[dim 16nb + 4g + j][query c] += V^T P^T over the chunk's 64 tokens.
+            // B element 4*(s%2)+j of step kk is token 32kk + 16(s%2) + 4g + j; the
+            // A operand takes the same tokens of dim 16nb + c.
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int d = 16 * nb + c;
+                const int sw = (d >> 3) & 15;
+                const _Float16* vrow = &vs[d * VTS];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(&vrow[4 * ((8 * kk + g) ^ sw)]);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(&vrow[4 * ((8 * kk + 4 + g) ^ sw)]);
+                    const h8 va = as_h8(u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                    for (int qt = 0; qt < QT; ++qt)
+                        o[qt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qt][kk], o[qt][nb],
+                                                                           0, 0, 0);
+                }
+            }
         }
     }
 
-    // O^T[column 16nb + 4g + j][query c] / l(query c)
-    if (c < n_rows) {
+    // ---- O^T[dim 16nb + 4g + j][query c] / l(query c) ----
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const float lsum = group_sum(lpart[qt]);
+        const int r = wr0 + 16 * qt + c;
+        if (r >= n_rows)
+            continue;
         const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
         if constexpr (kCascade) {
-            const int64_t u = ((int64_t)seq * P.num_heads + h) * P.num_slots + part;
+            const int64_t u = ((row0 + r) * P.num_heads + h) * P.num_slots + part;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                f4 r = o[nb] * inv;
-                *reinterpret_cast<f4*>(&P.ws_o[u * D + nb * 16 + 4 * g]) = r;
-            }
+            for (int nb = 0; nb < NB; ++nb)
+                *reinterpret_cast<f4*>(&P.ws_o[u * D + nb * 16 + 4 * g]) = o[qt][nb] * inv;
             if (g == 0) {
-                P.ws_m[u] = m;
+                P.ws_m[u] = m[qt];
                 P.ws_l[u] = lsum;
             }
         } else {
-            _Float16* orow = P.out + (q_row * P.num_heads + h) * D;
+            _Float16* orow = P.out + ((row0 + r) * P.num_heads + h) * D;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                h4 r;
+                typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+                h4 v;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    r[j] = (_Float16)(o[nb][j] * inv);
-                *reinterpret_cast<h4*>(&orow[nb * 16 + 4 * g]) = r;
+                    v[j] = (_Float16)(o[qt][nb][j] * inv);
+                *reinterpret_cast<h4*>(&orow[nb * 16 + 4 * g]) = v;
             }
         }
     }
@@ -256,15 +338,16 @@ __global__ __launch_bounds__(kWave) void pa_mq_kernel(MqParams P)
 template <bool kCascade>
 hipError_t launch_mq(const MqParams& P, int head_dim, int block_size, hipStream_t stream)
 {
-    const dim3 grid(P.total_units), block(kWave);
+    constexpr int QT = (kCascade ? kCascadeTileRows : kMqTileRows) / (kWaves * 16);
+    const dim3 grid(P.total_units), block(kMqThreads);
     if (head_dim == 128 && block_size == 16)
-        hipLaunchKernelGGL((pa_mq_kernel<128, 16, kCascade>), grid, block, 0, stream, P);
+        hipLaunchKernelGGL((pa_mq_kernel<128, 16, kCascade, QT>), grid, block, 0, stream, P);
     else if (head_dim == 128 && block_size == 32)
-        hipLaunchKernelGGL((pa_mq_kernel<128, 32, kCascade>), grid, block, 0, stream, P);
+        hipLaunchKernelGGL((pa_mq_kernel<128, 32, kCascade, QT>), grid, block, 0, stream, P);
     else if (head_dim == 64 && block_size == 16)
-        hipLaunchKernelGGL((pa_mq_kernel<64, 16, kCascade>), grid, block, 0, stream, P);
+        hipLaunchKernelGGL((pa_mq_kernel<64, 16, kCascade, QT>), grid, block, 0, stream, P);
     else if (head_dim == 64 && block_size == 32)
-        hipLaunchKernelGGL((pa_mq_kernel<64, 32, kCascade>), grid, block, 0, stream, P);
+        hipLaunchKernelGGL((pa_mq_kernel<64, 32, kCascade, QT>), grid, block, 0, stream, P);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
