@@ -176,7 +176,7 @@ MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 
 
 def bench_cascade(iters, warmup):
-    """Shared-prefix step (config 3) with the prefix read once per 16
+    """Shared-prefix step (config 3) with the prefix read once per 64
     sequences: reshape_and_cache + pa_decode_cascade."""
     import numpy as np
     import torch

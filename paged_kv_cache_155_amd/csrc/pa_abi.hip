@@ -178,9 +178,10 @@ bool valid_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 }  // namespace
 
 namespace {
-constexpr int32_t kPrefixPartLen = pa::kMqChunk;  // shared-prefix tokens per workgroup
+constexpr int32_t kPrefixPartLen = 2 * pa::kMqChunk;  // shared-prefix tokens per workgroup
 
 int32_t prefix_parts(int32_t prefix_len) { return (prefix_len + kPrefixPartLen - 1) / kPrefixPartLen; }
+
 }  // namespace
 
 size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
@@ -244,6 +245,9 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
     m.row_tiles = (int32_t)row_tiles;
     m.total_units = (uint32_t)(row_tiles * parts * num_heads);
     m.scale_log2 = p.scale_log2;
+    // Prefix pass first (slots 0..parts-1), then the suffix partitions; when
+    // every suffix fits one partition the partition kernel merges the prefix
+    // slots itself and writes the rows, else the reduce merges all slots.
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = pa::launch_cascade_prefix(m, head_dim, block_size, st);
     if (e == hipSuccess)

@@ -260,6 +260,30 @@ __device__ __forceinline__ void merge_into(LaneState<KV>& st, float m_o, float l
     st.m = M;
 }
 
+// Column d of a row whose shared-prefix partials sit in workspace slots
+// 0 .. slot_base-1 of u0 and whose one suffix partition has (M, L, o):
+// the log-sum-exp merge, prefix slots first, then the suffix (L = 0: none).
+template <int D>
+__device__ float merge_with_prefix(const DecodeParams& P, int64_t u0, int d, float M, float L,
+                                   float o)
+{
+    float Mx = M;
+    for (int p = 0; p < P.slot_base; ++p)
+        Mx = fmaxf(Mx, P.ws_m[u0 + p]);
+    float wsum = 0.0f, acc = 0.0f;
+    for (int p = 0; p < P.slot_base; ++p) {
+        const float w = P.ws_l[u0 + p] * exp2_fast(P.ws_m[u0 + p] - Mx);
+        wsum += w;
+        acc = fmaf(w, P.ws_o[(u0 + p) * D + d], acc);
+    }
+    if (L > 0.0f) {
+        const float w = L * exp2_fast(M - Mx);
+        wsum += w;
+        acc = fmaf(w, o, acc);
+    }
+    return acc / wsum;
+}
+
 template <typename KV, int D, int B>
 __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
 {
@@ -281,9 +305,15 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
     const int wave = threadIdx.x / kWave;
     const int64_t row = ((int64_t)s * P.num_heads + h) * D;
 
-    if (ctx <= 0) {  // empty context: zero row, written by partition 0 only
-        if (part == 0 && threadIdx.x < D && P.slot_base == 0)
-            P.out[row + threadIdx.x] = (_Float16)0.0f;
+    if (ctx <= 0) {  // empty context: partition 0 writes the row
+        if (part == 0 && threadIdx.x < D) {
+            if (P.slot_base == 0)
+                P.out[row + threadIdx.x] = (_Float16)0.0f;
+            else if (P.num_partitions == 1)  // the shared prefix alone
+                P.out[row + threadIdx.x] = (_Float16)merge_with_prefix<D>(
+                    P, ((int64_t)s * P.num_heads + h) * P.num_slots, threadIdx.x, kNegInf, 0.0f,
+                    0.0f);
+        }
         return;
     }
     if (p0 >= ctx)
@@ -376,6 +406,9 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
             o *= P.v_scale;
         if (nparts_seq == 1 && P.slot_base == 0) {
             P.out[row + d] = (_Float16)o;
+        } else if (P.slot_base > 0 && P.num_partitions == 1) {
+            P.out[row + d] = (_Float16)merge_with_prefix<D>(
+                P, ((int64_t)s * P.num_heads + h) * P.num_slots, d, M, L, o);
         } else {
             const int64_t u = ((int64_t)s * P.num_heads + h) * P.num_slots + P.slot_base + part;
             P.ws_o[u * D + d] = o;
@@ -388,104 +421,130 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
 }
 
 // Merge the partitions of one (sequence, head): M = max m_p,
-// w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p.  A workgroup of
-// 256 threads per (sequence, head): thread (g, d) sums column d over the
-// partitions p = g, g + G, ... (G = 256 / D groups), the groups are then
-// added in order g = 0, 1, ... - a fixed order, so the result is
-// deterministic.  Partitions are taken 256 at a time.
+// w_p = l_p * 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p.  One wave per
+// (sequence, head), four per workgroup.  Lane i takes the (m, l) of
+// partitions i, i + 64, ...; M and sum_p w_p come from fixed butterflies; each
+// lane owns D / 64 output columns and adds w_p o_p over the partitions in
+// order p = 0, 1, ... (the weight broadcast from its lane with v_readlane).
+// A fixed order, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
 {
-    constexpr int G = kThreads / D;
-    const int sh = blockIdx.x;
+    constexpr int CPL = D / kWave;  // output columns per lane
+    static_assert(CPL == 1 || CPL == 2, "head_dim 64 or 128");
+    const int lane = threadIdx.x % kWave;
+    const int sh = blockIdx.x * kWaves + threadIdx.x / kWave;
+    if (sh >= P.num_seqs * P.num_heads)
+        return;  // no barriers in this kernel
     const int s = sh / P.num_heads;
     const int ctx = P.context_lens[s];
-    // slots in use: the shared-prefix slot (if any) + this sequence's partitions
+    // slots in use: the shared-prefix slots (if any) + this sequence's partitions
     const int np = P.slot_base + (ctx + P.partition_size - 1) / P.partition_size;
     if (np == 0 || (np == 1 && P.slot_base == 0))
         return;  // nothing to merge (an unsplit sequence wrote its own row)
-    const int t = threadIdx.x;
-    const int lane = t % kWave;
-    const int wave = t / kWave;
-    const int g = t / D;
-    const int d = t % D;
     const int64_t u0 = (int64_t)sh * P.num_slots;
     const float* m = P.ws_m + u0;
     const float* l = P.ws_l + u0;
-    const float* o = P.ws_o + u0 * D;
-
-    __shared__ float s_red[kWaves];
-    __shared__ float s_w[kThreads];
-    __shared__ float s_acc[G][D];
 
     float M = kNegInf;
-    for (int p = t; p < np; p += kThreads)
+    for (int p = lane; p < np; p += kWave)
         M = fmaxf(M, m[p]);
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1)
         M = fmaxf(M, __shfl_xor(M, off));
-    if (lane == 0)
-        s_red[wave] = M;
-    __syncthreads();
-    M = s_red[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-        M = fmaxf(M, s_red[w]);
 
-    float acc = 0.0f, L = 0.0f;
-    for (int c0 = 0; c0 < np; c0 += kThreads) {
-        const int n = min(kThreads, np - c0);
-        __syncthreads();  // s_w of the previous chunk fully consumed
-        if (t < n)
-            s_w[t] = l[c0 + t] * exp2_fast(m[c0 + t] - M);
-        __syncthreads();
-        const float* oc = o + (int64_t)c0 * D + d;
-#pragma unroll 8
-        for (int p = g; p < n; p += G)
-            acc = fmaf(s_w[p], oc[(int64_t)p * D], acc);
-        if (t == 0)
-            for (int p = 0; p < n; ++p)
-                L += s_w[p];
-    }
-    s_acc[g][d] = acc;
-    if (t == 0)
-        s_red[0] = L;
-    __syncthreads();
-    if (t < D) {
-        float sum = s_acc[0][t];
+    float acc[CPL] = {};
+    float L = 0.0f;
+    for (int c0 = 0; c0 < np; c0 += kWave) {
+        const int p = c0 + lane;
+        const float w = p < np ? l[p] * exp2_fast(m[p] - M) : 0.0f;
+        float wsum = w;
 #pragma unroll
-        for (int gg = 1; gg < G; ++gg)
-            sum += s_acc[gg][t];
-        P.out[(int64_t)sh * D + t] = (_Float16)(sum / s_red[0]);
+        for (int off = 1; off < kWave; off <<= 1)
+            wsum += __shfl_xor(wsum, off);
+        L += wsum;
+        const int n = min(kWave, np - c0);
+        const float* oc = P.ws_o + (u0 + c0) * D + lane * CPL;
+        auto add = [&](int j) {
+            const float wj = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+            if constexpr (CPL == 2) {
+                const float2 o2 = *reinterpret_cast<const float2*>(oc + (int64_t)j * D);
+                acc[0] = fmaf(wj, o2.x, acc[0]);
+                acc[1] = fmaf(wj, o2.y, acc[1]);
+            } else {
+                acc[0] = fmaf(wj, oc[(int64_t)j * D], acc[0]);
+            }
+        };
+        int j = 0;
+        for (; j + 4 <= n; j += 4) {  // four independent loads in flight
+            add(j);
+            add(j + 1);
+            add(j + 2);
+            add(j + 3);
+        }
+        for (; j < n; ++j)
+            add(j);
     }
+    _Float16* orow = P.out + (int64_t)sh * D + lane * CPL;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+        orow[i] = (_Float16)(acc[i] / L);
 }
 
 template <typename KV, int D, int B>
-hipError_t launch_decode(const DecodeParams& P, hipStream_t stream)
+hipError_t launch_partitions(const DecodeParams& P, hipStream_t stream)
 {
     hipLaunchKernelGGL((pa_partition_kernel<KV, D, B>), dim3(P.total_units), dim3(kThreads), 0,
                        stream, P);
-    if (P.num_slots > 1)
-        hipLaunchKernelGGL((pa_reduce_kernel<D>), dim3(P.num_seqs * P.num_heads), dim3(kThreads),
-                           0, stream, P);
     return hipGetLastError();
+}
+
+template <typename KV>
+hipError_t dispatch_partitions(const DecodeParams& P, int head_dim, int block_size,
+                               hipStream_t stream)
+{
+    if (head_dim == 128 && block_size == 16)
+        return launch_partitions<KV, 128, 16>(P, stream);
+    if (head_dim == 128 && block_size == 32)
+        return launch_partitions<KV, 128, 32>(P, stream);
+    if (head_dim == 64 && block_size == 16)
+        return launch_partitions<KV, 64, 16>(P, stream);
+    if (head_dim == 64 && block_size == 32)
+        return launch_partitions<KV, 64, 32>(P, stream);
+    return hipErrorInvalidValue;
 }
 
 template <typename KV>
 hipError_t dispatch(const DecodeParams& P, int head_dim, int block_size, hipStream_t stream)
 {
-    if (head_dim == 128 && block_size == 16)
-        return launch_decode<KV, 128, 16>(P, stream);
-    if (head_dim == 128 && block_size == 32)
-        return launch_decode<KV, 128, 32>(P, stream);
-    if (head_dim == 64 && block_size == 16)
-        return launch_decode<KV, 64, 16>(P, stream);
-    if (head_dim == 64 && block_size == 32)
-        return launch_decode<KV, 64, 32>(P, stream);
-    return hipErrorInvalidValue;
+    hipError_t e = dispatch_partitions<KV>(P, head_dim, block_size, stream);
+    if (e == hipSuccess)
+        e = launch_decode_reduce(P, head_dim, stream);
+    return e;
 }
 
 }  // namespace
+
+hipError_t launch_decode_reduce(const DecodeParams& P, int head_dim, hipStream_t stream)
+{
+    if (P.num_partitions <= 1)
+        return hipSuccess;  // the partition kernel wrote every row
+    const dim3 grid((uint32_t)(((int64_t)P.num_seqs * P.num_heads + kWaves - 1) / kWaves));
+    if (head_dim == 128)
+        hipLaunchKernelGGL((pa_reduce_kernel<128>), grid, dim3(kThreads), 0, stream, P);
+    else if (head_dim == 64)
+        hipLaunchKernelGGL((pa_reduce_kernel<64>), grid, dim3(kThreads), 0, stream, P);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_partitions(const DecodeParams& P, int head_dim, int block_size,
+                                    hipStream_t stream)
+{
+    return dispatch_partitions<KvF16>(P, head_dim, block_size, stream);
+}
 
 hipError_t launch_decode_dispatch(const DecodeParams& P, int head_dim, int block_size,
                                   hipStream_t stream)

@@ -66,8 +66,14 @@ hipError_t launch_multiquery(const MqParams& p, int head_dim, int block_size, hi
 hipError_t launch_cascade_prefix(const MqParams& p, int head_dim, int block_size,
                                  hipStream_t stream);
 
+// partition kernel + (if num_slots > 1) the log-sum-exp reduce
 hipError_t launch_decode_dispatch(const DecodeParams& p, int head_dim, int block_size,
                                   hipStream_t stream);
+// the two halves of launch_decode_dispatch (fp16 cache), for callers that
+// order other work between them
+hipError_t launch_decode_partitions(const DecodeParams& p, int head_dim, int block_size,
+                                    hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeParams& p, int head_dim, hipStream_t stream);
 
 hipError_t launch_decode_fp8_dispatch(const DecodeParams& p, int head_dim, int block_size,
                                       hipStream_t stream);

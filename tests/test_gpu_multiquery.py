@@ -95,17 +95,22 @@ def test_cascade_matches_plain_decode(orc, kw, P):
     log(f"[cascade] max abs err {ea:.3e}")
 
 
-def test_cascade_suffix_edges(orc):
+@pytest.mark.parametrize("prefix_blocks,B", [(4, 16), (9, 16), (5, 32)],
+                         ids=["prefix64_B16", "prefix144_B16", "prefix160_B32"])
+def test_cascade_suffix_edges(orc, prefix_blocks, B):
     """Suffixes of length 0 (the whole context is the prefix), 1, and a
-    block and a partition boundary; a batch size that is not a multiple of 16."""
+    block and a partition boundary; a batch size that is not a multiple of 16;
+    prefixes that end inside a 64-token chunk and inside a prefix partition.
+    P = 0 puts every suffix in one partition (the partition kernel merges the
+    prefix slots), P = 16 and 512 go through the reduce."""
     import torch
     import paged_kv_cache_155_amd as pa
     from paged_kv_cache_155_amd.workloads import make_random
-    log("[cascade] suffix edges")
-    prefix_blocks = 4
+    log(f"[cascade] suffix edges prefix {prefix_blocks} blocks of {B}")
     suffix = [0, 1, 15, 16, 17, 511, 512, 513, 0, 40, 3, 100, 64, 65, 2, 1, 0, 300]
     S = len(suffix)
-    w = make_random([prefix_blocks * 16 + x for x in suffix], 2, 128, 16, seed=41, poison=True)
+    plen = prefix_blocks * B
+    w = make_random([plen + x for x in suffix], 2, 128, B, seed=41 + B, poison=True)
     w.block_tables[:, :prefix_blocks] = w.block_tables[0, :prefix_blocks]
     kc, vc = w.k_cache.copy(), w.v_cache.copy()
     ok = w.slot_mapping >= 0
@@ -115,10 +120,9 @@ def test_cascade_suffix_edges(orc):
     prefix = w.block_tables[0, :prefix_blocks].astype(np.int32)
     st = np.ascontiguousarray(w.block_tables[:, prefix_blocks:])
     sl = np.array(suffix, dtype=np.int32)
-    for P in (0, 16, 512):
+    for P in (0, B, 512):
         out = to_dev(np.full((S, 2, 128), np.nan, dtype=np.float16))
         pa.decode_cascade(out, to_dev(w.q), to_dev(kc), to_dev(vc), to_dev(prefix),
-                          prefix_blocks * 16, to_dev(st), to_dev(sl), float(w.scale),
-                          partition_size=P)
+                          plen, to_dev(st), to_dev(sl), float(w.scale), partition_size=P)
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), ref, f"cascade edges P={P}")
