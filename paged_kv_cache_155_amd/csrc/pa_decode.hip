@@ -425,7 +425,8 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
 // (sequence, head), four per workgroup.  Lane i takes the (m, l) of
 // partitions i, i + 64, ...; M and sum_p w_p come from fixed butterflies; each
 // lane owns D / 64 output columns and adds w_p o_p over the partitions in
-// order p = 0, 1, ... (the weight broadcast from its lane with v_readlane).
+// order p = 0, 1, ... (the weight broadcast from its lane with v_readlane),
+// up to sixteen slot loads in flight.
 // A fixed order, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
@@ -477,11 +478,15 @@ __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
             }
         };
         int j = 0;
-        for (; j + 4 <= n; j += 4) {  // four independent loads in flight
-            add(j);
-            add(j + 1);
-            add(j + 2);
-            add(j + 3);
+        for (; j + 16 <= n; j += 16) {  // sixteen independent loads in flight
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                add(j + k);
+        }
+        for (; j + 4 <= n; j += 4) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                add(j + k);
         }
         for (; j < n; ++j)
             add(j);

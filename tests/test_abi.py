@@ -124,3 +124,76 @@ def test_fp8_rejects(lib):
     bad = list(args)
     bad[15] = 24    # partition size
     assert g(*bad) == -4
+
+
+def test_cascade_workspace_size(lib):
+    import paged_kv_cache_155_amd as pa
+    r = lambda b: (b + 255) // 256 * 256
+    # no prefix: the plain decode's workspace
+    assert (pa.decode_cascade_workspace_size(8, 32, 128, 16, 0, 128, 512)
+            == pa.decode_workspace_size(8, 32, 128, 16, 128, 512))
+    # 512-token prefix in 128-token pieces (4 slots) + one suffix partition
+    units = 8 * 32 * (4 + 1)
+    assert pa.decode_cascade_workspace_size(8, 32, 128, 16, 512, 32, 0) == (
+        r(units * 128 * 4) + 2 * r(units * 4))
+    # a prefix ending inside a piece still takes a slot; suffix split in 4
+    units = 8 * 32 * (2 + 4)
+    assert pa.decode_cascade_workspace_size(8, 32, 128, 16, 144, 128, 512) == (
+        r(units * 128 * 4) + 2 * r(units * 4))
+    assert pa.decode_cascade_workspace_size(8, 32, 128, 16, -16, 32, 0) == 0
+    assert pa.decode_cascade_workspace_size(8, 32, 128, 16, 512, 32, 24) == 0
+
+
+def _cascade(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, pt=FAKE, plen=64, bt=FAKE, cl=FAKE, S=2, H=4,
+             D=128, NB=8, B=16, MB=4, scale=0.088, P=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.pa_decode_cascade(a["out"], a["q"], a["k"], a["v"], a["pt"], a["plen"], a["bt"],
+                                 a["cl"], a["S"], a["H"], a["D"], a["NB"], a["B"], a["MB"],
+                                 a["scale"], a["P"], a["ws"], a["wsb"], None)
+
+
+def test_cascade_rejects(lib):
+    # every call below must fail validation (or have nothing to do): the pointers are fake
+    assert _cascade(lib, plen=17) == -2              # not a multiple of block_size
+    assert _cascade(lib, plen=-16) == -2
+    assert _cascade(lib, scale=0.0) == -2            # the MFMA pass needs scale > 0
+    assert _cascade(lib, scale=-0.088) == -2
+    assert _cascade(lib, scale=float("nan")) == -2
+    assert _cascade(lib, D=96) == -3
+    assert _cascade(lib, B=8, plen=64) == -3
+    assert _cascade(lib, P=24) == -4
+    assert _cascade(lib, wsb=16) == -5               # prefix slots need a workspace
+    assert _cascade(lib, q=P(0x10008)) == -6
+    assert _cascade(lib, out=P(0)) == -1
+    assert _cascade(lib, pt=P(0)) == -1              # checked after the decode arguments
+    assert _cascade(lib, plen=0, D=96) == -3         # no prefix: pa_decode's checks
+    assert _cascade(lib, S=0, out=P(0), pt=P(0)) == 0  # nothing to do
+
+
+def _mq(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, S=2, T=10, maxq=8,
+             H=4, D=128, NB=8, B=16, MB=4, scale=0.088)
+    a.update(kw)
+    return lib.pa_multi_query(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"],
+                              a["S"], a["T"], a["maxq"], a["H"], a["D"], a["NB"], a["B"], a["MB"],
+                              a["scale"], None)
+
+
+def test_multi_query_rejects(lib):
+    # every call below must fail validation (or have nothing to do): the pointers are fake
+    assert _mq(lib, S=-1) == -2
+    assert _mq(lib, T=-1) == -2
+    assert _mq(lib, maxq=-1) == -2
+    assert _mq(lib, H=0) == -2
+    assert _mq(lib, D=96) == -3
+    assert _mq(lib, B=8) == -3
+    assert _mq(lib, scale=0.0) == -2
+    assert _mq(lib, scale=float("inf")) == -2
+    assert _mq(lib, qs=P(0)) == -1
+    assert _mq(lib, out=P(0)) == -1
+    assert _mq(lib, q=P(0x10004)) == -6
+    assert _mq(lib, qs=P(0x10002)) == -6
+    assert _mq(lib, S=0, out=P(0)) == 0
+    assert _mq(lib, T=0, out=P(0)) == 0
+    assert _mq(lib, maxq=0, out=P(0)) == 0
