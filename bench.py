@@ -47,7 +47,9 @@ def _args():
     ap.add_argument("--cpu-sample-tokens", type=float, default=1.0e7,
                     help="cap on token-heads of oracle work in the CPU baseline sample")
     ap.add_argument("--cpu-repeats", type=int, default=3,
-                    help="oracle runs over the sample (the median is reported)")
+                    help="least number of timed oracle runs of the sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="keep repeating the oracle sample until this much wall time is spent")
     ap.add_argument("--op", choices=["step", "copy_blocks", "swap", "cascade", "multi_query"],
                     default="step",
                     help="step: the decode step (default); copy_blocks / swap: the block "
@@ -175,7 +177,7 @@ def bench_blocks(op, pairs, iters):
 MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 
 
-def bench_cascade(iters, warmup):
+def bench_cascade(iters, warmup, cpu=None):
     """Shared-prefix step (config 3) with the prefix read once per 64
     sequences: reshape_and_cache + pa_decode_cascade."""
     import numpy as np
@@ -214,6 +216,20 @@ def bench_cascade(iters, warmup):
     dec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     rc = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     uniq, logical = w.unique_kv_bytes(), w.kv_bytes()
+    line_cpu = None
+    if cpu is not None:  # the oracle's decode over the full tables, whole workload
+        import oracle
+        orc = oracle.get()
+        okc, ovc = w.k_cache.copy(), w.v_cache.copy()
+        orc.reshape_and_cache(w.key, w.value, okc, ovc, w.slot_mapping)
+        dt, runs = _time_oracle(lambda: orc.decode(w.q, okc, ovc, w.block_tables, w.context_lens,
+                                                   scale), cpu.cpu_repeats, cpu.cpu_seconds)
+        line_cpu = {"value": round(uniq / dt / 1e9, 4), "unit": "GB/s (unique K/V bytes)",
+                    "cores": orc.threads_used, "kind": "oracle",
+                    "sample": f"the whole workload ({w.num_seqs} seqs x {w.num_heads} heads over "
+                              f"the full tables); fp64 oracle decode, median of {runs} runs = "
+                              f"{dt:.3f} s wall on {orc.threads_used} threads; "
+                              f"{w.num_seqs / dt:.1f} tokens/s/layer"}
     print(json.dumps({
         "op": "cascade", "workload": f"config3: {DESCRIPTIONS[3]}", "partition_size": P,
         "t_decode_us_mean": round(dec * 1e3, 2), "t_reshape_us_mean": round(rc * 1e3, 2),
@@ -224,10 +240,11 @@ def bench_cascade(iters, warmup):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(uniq / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "bytes": "unique K/V bytes"},
-        "logical_kv_gbs": round(logical / (dec * 1e-3) / 1e9, 1)}), flush=True)
+        "logical_kv_gbs": round(logical / (dec * 1e-3) / 1e9, 1),
+        "cpu_baseline": line_cpu}), flush=True)
 
 
-def bench_multi_query(iters, warmup):
+def bench_multi_query(iters, warmup, cpu=None):
     """A chunked-prefill batch: 16 sequences of 2048 positions whose last 512
     are this step's new tokens (32 heads x 128, B = 16)."""
     import numpy as np
@@ -250,6 +267,21 @@ def bench_multi_query(iters, warmup):
     visible = sum(ctx - n + i + 1 for i in range(n)) * S          # (row, key) pairs per head
     flops = 4.0 * D * visible * H                                   # q.k and p.v
     kv_unique = S * ctx * H * D * 2 * 2
+    line_cpu = None
+    if cpu is not None:  # the oracle's prefill on the first 2 of the 16 sequences
+        import oracle
+        orc = oracle.get()
+        ns = 2
+        sq = qh[qs[0]:qs[ns]]
+        dt, runs = _time_oracle(lambda: orc.prefill(sq, w.k_cache, w.v_cache, w.block_tables[:ns],
+                                                    w.context_lens[:ns], qs[:ns + 1], scale),
+                                cpu.cpu_repeats, cpu.cpu_seconds)
+        sflops = flops * ns / S
+        line_cpu = {"value": round(sflops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": orc.threads_used,
+                    "kind": "oracle",
+                    "sample": f"{ns} of {S} sequences ({ns * n} query rows x {H} heads); fp64 "
+                              f"oracle prefill, median of {runs} runs = {dt:.3f} s wall on "
+                              f"{orc.threads_used} threads; {ns * n / dt:.1f} query rows/s"}
     print(json.dumps({
         "op": "multi_query", "workload": f"{S} seqs x {ctx} positions, last {n} new, 32 heads x 128",
         "rows": S * n, "us_median": round(t * 1e6, 2),
@@ -257,13 +289,26 @@ def bench_multi_query(iters, warmup):
         "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 2),
                      "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / t / 1e12 / MFMA_F16_TFLOPS, 4)},
-        "kv_unique_gbs": round(kv_unique / t / 1e9, 1)}), flush=True)
+        "kv_unique_gbs": round(kv_unique / t / 1e9, 1), "cpu_baseline": line_cpu}), flush=True)
 
 
-def cpu_baseline(w, sample_tokens, repeats):
+def _time_oracle(fn, repeats, seconds):
+    """Median wall time of fn() over at least `repeats` runs, repeated until
+    `seconds` of wall time are spent (capped at 1000 runs)."""
+    import numpy as np
+    times = []
+    while len(times) < max(1, repeats) or (sum(times) < seconds and len(times) < 1000):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), len(times)
+
+
+def cpu_baseline(w, sample_tokens, repeats, seconds):
     """Time the oracle (as it stands) on a bounded, deterministic sample of
     (sequence, head) pairs of the same workload (the whole workload when it
-    is under the cap); GB/s over the sampled K/V bytes, median of repeats."""
+    is under the cap); GB/s over the sampled K/V bytes, median of the runs
+    (at least `repeats`, and more until `seconds` of wall time are spent)."""
     import numpy as np
     import oracle
     from paged_kv_cache_155_amd.workloads import kv_bytes_per_token
@@ -281,18 +326,15 @@ def cpu_baseline(w, sample_tokens, repeats):
         s, h = pairs[i]
         chosen.append((s, h))
         tok += int(w.context_lens[s])
-    times = []
-    for _ in range(max(1, repeats)):
-        t0 = time.perf_counter()
-        orc.decode_pairs(chosen, w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale))
-        times.append(time.perf_counter() - t0)
-    dt = float(np.median(times))
+    dt, runs = _time_oracle(lambda: orc.decode_pairs(chosen, w.q, kc, vc, w.block_tables,
+                                                      w.context_lens, float(w.scale)),
+                            repeats, seconds)
     nbytes = tok * kv_bytes_per_token(1, w.head_dim)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": orc.threads_used,
             "kind": "oracle",
             "sample": f"{len(chosen)} of {len(pairs)} (sequence, head) pairs (seeded permutation), "
                       f"{tok} token-heads = {nbytes} K/V bytes; fp64 oracle decode, median of "
-                      f"{len(times)} runs = {dt:.3f} s wall on {orc.threads_used} threads; "
+                      f"{runs} runs = {dt:.3f} s wall on {orc.threads_used} threads; "
                       f"tokens/s/layer-equivalent {len(chosen) / H / dt:.1f}"}
 
 
@@ -317,10 +359,10 @@ def main():
         probe_copy(a.probe_mib)
         return
     if a.op == "cascade":
-        bench_cascade(a.steps, a.warmup)
+        bench_cascade(a.steps, a.warmup, None if a.no_cpu_baseline else a)
         return
     if a.op == "multi_query":
-        bench_multi_query(a.steps, a.warmup)
+        bench_multi_query(a.steps, a.warmup, None if a.no_cpu_baseline else a)
         return
     if a.op != "step":
         bench_blocks(a.op, a.pairs, a.steps)
@@ -424,7 +466,7 @@ def main():
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline and not fp8:
-        line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens, a.cpu_repeats)
+        line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens, a.cpu_repeats, a.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
