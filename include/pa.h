@@ -189,7 +189,7 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
  *   block_tables, context_lens  as pa_decode; n_s <= context_lens[s]
  *   scale          finite and > 0 (else PA_ERR_INVALID_DIM)
  * head_dim 64 or 128, block_size 16 or 32.  No workspace.  Rows are
- * processed in tiles of 64 per (sequence, head); a K/V chunk of 64 tokens is
+ * processed in tiles of 128 per (sequence, head); a K/V chunk of 64 tokens is
  * read once per tile.
  */
 int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,

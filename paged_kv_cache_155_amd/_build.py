@@ -18,8 +18,12 @@ LIB = os.path.join(PKG, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
+# -amdgpu-mfma-vgpr-form: matrix-core accumulators in VGPRs.  The multi-query
+# kernel keeps its softmax state and rescales O with VALU ops, and the AGPR form
+# made the compiler copy S and O between the register files on every chunk.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -33,7 +33,7 @@ struct DecodeParams {
 // Several query rows against one K/V token stream (multi-query / shared prefix).
 constexpr int kMqThreads = 256;       // threads per workgroup (4 waves)
 constexpr int kMqChunk = 64;          // tokens staged in LDS per step
-constexpr int kMqTileRows = 64;       // multi-query rows per workgroup
+constexpr int kMqTileRows = 128;      // multi-query rows per workgroup (32 per wave)
 constexpr int kCascadeTileRows = 64;  // shared-prefix sequences per workgroup
 
 struct MqParams {

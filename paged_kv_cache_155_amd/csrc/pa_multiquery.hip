@@ -21,12 +21,10 @@
 //
 // Per 64-token chunk of the stream:
 //   * the 256 threads load it once (each: 4 consecutive tokens x 8 dims of
-//     K and of V, 16-byte loads through the block table) and stage it in LDS,
-//     double buffered so one barrier per chunk suffices; K keeps its row
-//     layout, V is transposed on the way in (4 x 8 halves per thread, 8-byte
-//     stores into rows of 72 halves with the 4-token group XOR-swizzled by
-//     dim / 8, which keeps both the stores and the MFMA-operand reads free of
-//     bank conflicts); the next chunk's loads are issued before the math;
+//     K and of V, 16-byte loads through the block table) and stage it in LDS
+//     in its row layout (rows padded to D+8 halves for K, D+16 for V), double
+//     buffered so one barrier per chunk suffices; the next chunk's loads are
+//     issued before the math;
 //   * each wave, for its 16 * QT rows:
 //       S^T = K Q^T      v_mfma_f32_16x16x32_f16 over the head dim (each lane
 //                        group owns a contiguous quarter of the dims, so K and
@@ -37,7 +35,11 @@
 //                        sum stays per lane until the end; O is rescaled only
 //                        when some row's max moved
 //       O^T += V^T P^T   v_mfma_f32_16x16x32_f16 over 32 tokens; the S^T
-//                        tiles are already P^T in the B-operand layout
+//                        tiles are already P^T in the B-operand layout, and
+//                        the V^T operand comes from the transposing LDS read
+//                        ds_read_b64_tr_b16 on the row-layout V tile (the
+//                        D+16 stride keeps its 16-lane groups on distinct
+//                        banks)
 // Positions past a row's limit get -inf scores; K/V rows past the stream end
 // are loaded as zeros (select, not multiply), so unread slots may hold
 // anything.
@@ -61,6 +63,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ h8 as_h8(const u32x4& v) { return __builtin_bit_cast(h8, v); }
+
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
+// ds_read_b64_tr_b16 (transposing LDS read; 8-byte aligned LDS address)
+__device__ __forceinline__ s4 ds_read_tr16(const _Float16* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
+}
 
 // max / sum over the four 16-lane groups (lanes c, c+16, c+32, c+48)
 __device__ __forceinline__ float group_max(float x)
@@ -95,7 +105,7 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     constexpr int NB = D / 16;            // 16-dim blocks of O^T
     constexpr int KI = D / 32;            // MFMA k-steps over the head dim
     constexpr int KS = D + 8;             // LDS row stride (halves) of the K tile
-    constexpr int VTS = N + 8;            // LDS row stride (halves) of the V^T tile
+    constexpr int VS = D + 16;            // LDS row stride (halves) of the V tile
     constexpr int WROWS = 16 * QT;        // query rows per wave
     constexpr int ROWS = kWaves * WROWS;  // query rows per workgroup
     constexpr int DG = D / 8;             // 8-dim groups per token row
@@ -105,7 +115,7 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     static_assert(ROWS == (kCascade ? kCascadeTileRows : kMqTileRows), "tile rows");
 
     __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][N * KS];  // [token][dim]
-    __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][D * VTS]; // [dim][token (swizzled)]
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][N * VS];  // [token][dim]
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
@@ -203,17 +213,9 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
         _Float16* vs = v_lds[buf];
         if (loader) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
                 *reinterpret_cast<u32x4*>(&ks[(4 * lq + j) * KS + 8 * lp]) = kr[j];
-            // V^T: dim 8lp+e, tokens 4lq..4lq+3 -> one 8-byte store per dim
-            const int col = 4 * (lq ^ lp);  // swizzle (dim / 8) % 16 == lp
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t a = vr[0][w], b = vr[1][w], cc = vr[2][w], d = vr[3][w];
-                const u32x2 even{(a & 0xffffu) | (b << 16), (cc & 0xffffu) | (d << 16)};
-                const u32x2 odd{(a >> 16) | (b & 0xffff0000u), (cc >> 16) | (d & 0xffff0000u)};
-                *reinterpret_cast<u32x2*>(&vs[(8 * lp + 2 * w) * VTS + col]) = even;
-                *reinterpret_cast<u32x2*>(&vs[(8 * lp + 2 * w + 1) * VTS + col]) = odd;
+                *reinterpret_cast<u32x4*>(&vs[(4 * lq + j) * VS + 8 * lp]) = vr[j];
             }
         }
         if (t0 + N < stream_end)
@@ -283,17 +285,21 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
 
             // O^T[dim 16nb + 4g + j][query c] += V^T P^T over the chunk's 64 tokens.
             // B element 4*(s%2)+j of step kk is token 32kk + 16(s%2) + 4g + j; the
-            // A operand takes the same tokens of dim 16nb + c.
+            // A operand takes the same tokens of dim 16nb + c, read with the
+            // transposing LDS load: in each 16-lane group, lane i gets element
+            // i%4 of the 8 bytes addressed by lane 4e + i/4 as its element e, so
+            // lane (c, g) addresses token 32kk + 16h + 4g + c/4, dims
+            // 16nb + 4(c%4) .. +3, and receives 4 tokens of dim 16nb + c.
+            const _Float16* vsrc = &vs[(4 * g + c / 4) * VS + 4 * (c % 4)];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int d = 16 * nb + c;
-                const int sw = (d >> 3) & 15;
-                const _Float16* vrow = &vs[d * VTS];
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(&vrow[4 * ((8 * kk + g) ^ sw)]);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(&vrow[4 * ((8 * kk + 4 + g) ^ sw)]);
-                    const h8 va = as_h8(u32x4{lo.x, lo.y, hi.x, hi.y});
+                    const s4 lo = ds_read_tr16(&vsrc[(32 * kk) * VS + 16 * nb]);
+                    const s4 hi = ds_read_tr16(&vsrc[(32 * kk + 16) * VS + 16 * nb]);
+                    const h8 va = __builtin_bit_cast(
+                        h8, u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                                  __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y});
 #pragma unroll
                     for (int qt = 0; qt < QT; ++qt)
                         o[qt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qt][kk], o[qt][nb],
