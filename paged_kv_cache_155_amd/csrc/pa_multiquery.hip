@@ -193,16 +193,26 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     u32x4 kr[4], vr[4];
     auto load_chunk = [&](int t0) {
         const int t = t0 + 4 * lq;
-        const bool any = loader && t < stream_end;
-        const int64_t base = any ? (int64_t)table[t / B] * block_elems +
-                                       (int64_t)(t % B) * token_stride + h * D + 8 * lp
-                                 : 0;
+        if (!loader)
+            return;  // (only when D < 128: these threads stage nothing)
+        const int64_t base = t < stream_end ? (int64_t)table[t / B] * block_elems +
+                                                  (int64_t)(t % B) * token_stride + h * D + 8 * lp
+                                            : 0;
+        if (t + 4 <= stream_end) {  // all four tokens exist: no selects
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool ok = any && t + j < stream_end;
-            const int64_t e = base + (int64_t)j * token_stride;
-            kr[j] = ok ? *reinterpret_cast<const u32x4*>(P.k_cache + e) : u32x4{0, 0, 0, 0};
-            vr[j] = ok ? *reinterpret_cast<const u32x4*>(P.v_cache + e) : u32x4{0, 0, 0, 0};
+            for (int j = 0; j < 4; ++j) {
+                const int64_t e = base + (int64_t)j * token_stride;
+                kr[j] = *reinterpret_cast<const u32x4*>(P.k_cache + e);
+                vr[j] = *reinterpret_cast<const u32x4*>(P.v_cache + e);
+            }
+        } else {  // the stream ends inside this group: zeros past the end
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool ok = t + j < stream_end;
+                const int64_t e = base + (int64_t)j * token_stride;
+                kr[j] = ok ? *reinterpret_cast<const u32x4*>(P.k_cache + e) : u32x4{0, 0, 0, 0};
+                vr[j] = ok ? *reinterpret_cast<const u32x4*>(P.v_cache + e) : u32x4{0, 0, 0, 0};
+            }
         }
     };
 
@@ -242,8 +252,22 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
                 }
             }
 
+            // positions at or past a row's limit: -inf (only in chunks that
+            // cross some row's limit; a wave-uniform branch)
+            if (__builtin_amdgcn_readfirstlane((int)(t0 + N > wave_lo))) {
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) {
+                    const int nvis = lim[qt] - t0 - 4 * g;  // visible offsets 16s + j < nvis
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (16 * s + j >= nvis)
+                                st[qt][s][j] = kNegInf;
+                }
+            }
+
             // online softmax per query column; P^T as the B operand of the next product
-            const bool need_mask = t0 + N > wave_lo;
             h8 pb[QT][2];
             bool moved = false;
             float alpha[QT];
@@ -253,11 +277,8 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if (need_mask && t0 + 16 * s + 4 * g + j >= lim[qt])
-                            st[qt][s][j] = kNegInf;
+                    for (int j = 0; j < 4; ++j)
                         bmax = fmaxf(bmax, st[qt][s][j]);
-                    }
                 // scale > 0, so the max of the raw scores gives the max of the scaled ones
                 const float m_new = fmaxf(m[qt], group_max(bmax) * P.scale_log2);
                 const float m_ref = m_new == kNegInf ? 0.0f : m_new;
