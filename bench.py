@@ -17,12 +17,17 @@ against the 8 TB/s HBM3E peak.  cpu_baseline: the CPU oracle timed on a
 bounded sample of the same workload on the host cores.
 
 `--probe copy` instead runs a plain copy of known size (reshape_and_cache
-over 1 GiB) for calibrating hardware byte counters.
+over 1 GiB) for calibrating hardware byte counters; `--probe read` runs the
+streaming-read probe (read_probe.hip, built by __graft_entry__.build()) whose
+best rate is the achievable-peak figure the roofline also reports against.
+`--flush` evicts the L2s and the MALL (a 1 GiB write) before every timed step
+and times the steps by HIP events instead.
 """
 import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -57,7 +62,9 @@ def _args():
                          "cascade: the shared-prefix step through pa_decode_cascade (config "
                          "3); multi_query: a chunked-prefill batch through pa_multi_query")
     ap.add_argument("--pairs", type=int, default=1024, help="blocks per copy/swap call")
-    ap.add_argument("--probe", choices=["copy"], default=None)
+    ap.add_argument("--probe", choices=["copy", "read"], default=None)
+    ap.add_argument("--flush", action="store_true",
+                    help="write 1 GiB before each timed step (evicts L2 and MALL)")
     ap.add_argument("--probe-mib", type=int, default=1024)
     return ap.parse_args()
 
@@ -292,6 +299,39 @@ def bench_multi_query(iters, warmup, cpu=None):
         "kv_unique_gbs": round(kv_unique / t / 1e9, 1), "cpu_baseline": line_cpu}), flush=True)
 
 
+READ_PROBE = os.path.join(ROOT, "_build", "read_probe")
+READ_PEAK = os.path.join(ROOT, "profiles", "read_peak.json")
+
+
+def probe_read():
+    if not os.path.exists(READ_PROBE):
+        print(f"{READ_PROBE} is missing: run __graft_entry__.build() first", file=sys.stderr)
+        return 1
+    r = subprocess.run([READ_PROBE], capture_output=True, text=True, timeout=600)
+    sys.stdout.write(r.stdout)
+    sys.stderr.write(r.stderr)
+    return r.returncode
+
+
+def _measured_peak():
+    """Best streaming-read rate of read_probe.hip on this GPU type, as
+    committed in profiles/read_peak.json (None if absent)."""
+    try:
+        return float(json.load(open(READ_PEAK))["best_read_gbs"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _time_oracle(fn, repeats, seconds):
     """Median wall time of fn() over at least `repeats` runs, repeated until
     `seconds` of wall time are spent (capped at 1000 runs)."""
@@ -329,12 +369,27 @@ def cpu_baseline(w, sample_tokens, repeats, seconds):
     dt, runs = _time_oracle(lambda: orc.decode_pairs(chosen, w.q, kc, vc, w.block_tables,
                                                       w.context_lens, float(w.scale)),
                             repeats, seconds)
+    threads = orc.threads_used
+    # one core, on every 16th pair of the same sample
+    one = chosen[::16]
+    one_tok = sum(int(w.context_lens[s]) for s, _ in one)
+    orc.set_threads(1)
+    try:
+        dt1, runs1 = _time_oracle(lambda: orc.decode_pairs(one, w.q, kc, vc, w.block_tables,
+                                                            w.context_lens, float(w.scale)),
+                                  repeats, seconds / 4)
+    finally:
+        orc.set_threads(0)
     nbytes = tok * kv_bytes_per_token(1, w.head_dim)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": orc.threads_used,
-            "kind": "oracle",
+    one_bytes = one_tok * kv_bytes_per_token(1, w.head_dim)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "value_1core": round(one_bytes / dt1 / 1e9, 4),
+            "cpu": _cpu_model(),
             "sample": f"{len(chosen)} of {len(pairs)} (sequence, head) pairs (seeded permutation), "
                       f"{tok} token-heads = {nbytes} K/V bytes; fp64 oracle decode, median of "
-                      f"{runs} runs = {dt:.3f} s wall on {orc.threads_used} threads; "
+                      f"{runs} runs = {dt:.3f} s wall on {threads} threads; "
+                      f"value_1core: every 16th of those pairs on 1 thread, median of {runs1} "
+                      f"runs = {dt1:.3f} s; "
                       f"tokens/s/layer-equivalent {len(chosen) / H / dt:.1f}"}
 
 
@@ -346,6 +401,8 @@ def main():
               "this library is a single-GPU kernel; sharding is described, not built.",
               file=sys.stderr)
         sys.exit(2)
+    if a.probe == "read":  # a child process of its own; nothing here touches the GPU
+        sys.exit(probe_read())
     import numpy as np
     import torch
     import paged_kv_cache_155_amd as pa
@@ -412,6 +469,7 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if a.flush else None
 
     K = a.steps
     stream = torch.cuda.current_stream()
@@ -422,6 +480,8 @@ def main():
     wall0 = time.perf_counter()
     t_begin.record(stream)
     for i in range(K):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)  # evict the L2s and the 256 MB MALL
         ev[i][0].record(stream)
         write()
         ev[i][1].record(stream)
@@ -436,6 +496,8 @@ def main():
     ms_step = total_ms / K
     t_dec = float(np.mean(dec_ms))
     t_rc = float(np.mean(rc_ms))
+    if scratch is not None:  # the flushes are not part of a step
+        ms_step = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
     kvb = w.kv_bytes() // 2 if fp8 else w.kv_bytes()
     achieved = kvb / (t_dec * 1e-3) / 1e9
     value = kvb / (ms_step * 1e-3) / 1e9
@@ -456,10 +518,13 @@ def main():
             "t_decode_us_mean": round(t_dec * 1e3, 2),
             "t_decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
             "t_reshape_us_mean": round(t_rc * 1e3, 2),
-            "wall_s_timed": round(wall, 4), "accumulate": "f32",
+            "wall_s_timed": round(wall, 4), "accumulate": "f32", "flush": bool(a.flush),
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "measured_peak": _measured_peak(),
+                     "frac_of_measured": (round(achieved / _measured_peak(), 4)
+                                          if _measured_peak() else None),
                      "traffic": None if fp8 else _traffic(f"config{a.config}_B{w.block_size}_P{P}"),
                      "kernel": ("pa_decode_fp8" if fp8 else "pa_decode")
                                + " (partition kernel + reduce kernel), HIP events"},

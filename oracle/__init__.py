@@ -69,8 +69,15 @@ class Oracle:
         lib.oracle_decode_fp8_pairs.restype = ctypes.c_int
         lib.oracle_prefill.argtypes = [_P] * 7 + [_I32] * 7 + [ctypes.c_double, _P]
         lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = ctypes.c_int
         self.lib = lib
         self.threads_used = 1
+
+    def set_threads(self, n):
+        """Host threads for later calls (n <= 0: the OpenMP default); timing
+        plumbing only.  Returns the count now in effect."""
+        return int(self.lib.oracle_set_threads(int(n)))
 
     # -- binary16 decoding -------------------------------------------------
     def half_to_double(self, bits):

@@ -606,3 +606,14 @@ int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
         *threads_used = nthreads;
     return status;
 }
+
+/* Timing plumbing, no arithmetic: the number of host threads later calls use
+ * (n <= 0: the OpenMP default).  Returns the count now in effect. */
+int oracle_set_threads(int n)
+{
+    static int default_threads = 0;
+    if (default_threads == 0)
+        default_threads = omp_get_max_threads();
+    omp_set_num_threads(n > 0 ? n : default_threads);
+    return omp_get_max_threads();
+}

@@ -40,5 +40,24 @@ def build(out=LIB, extra=(), quiet=False):
     return out
 
 
+PROBE_SRC = os.path.join(ROOT, "read_probe.hip")
+PROBE = os.path.join(ROOT, "_build", "read_probe")
+
+
+def build_probe(quiet=False):
+    """The streaming-read probe that bench.py --probe read runs (not part of
+    the library)."""
+    os.makedirs(os.path.dirname(PROBE), exist_ok=True)
+    cmd = [HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-o", PROBE + ".tmp", PROBE_SRC]
+    if not quiet:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(PROBE + ".tmp", PROBE)
+    return PROBE
+
+
 if __name__ == "__main__":
     build(quiet="-q" in sys.argv)
+    build_probe(quiet="-q" in sys.argv)

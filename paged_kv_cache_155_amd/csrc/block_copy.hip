@@ -8,8 +8,10 @@
 //
 // copy_blocks: a block is B*H*D fp16 values stored contiguously, so each
 // pair is one contiguous run per cache.  The grid has kChunks workgroups per
-// pair; a workgroup moves kVecsPerWg 16-byte vectors of K and of V (plain
-// loads and stores: the copy is read soon after by the decode).  Bit-exact,
+// pair; a workgroup moves kVecsPerWg 16-byte vectors of K and of V, all of
+// a thread's loads in flight before its stores (nontemporal loads: the
+// source is read once; plain stores: the copy is read soon after by the
+// decode).  Bit-exact,
 // no conversion.  Pure HBM copy: 2 * block bytes read and written per pair.
 //
 // swap_blocks: when both caches are reachable from the GPU (device memory,
@@ -48,9 +50,26 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     const u32x4* vs = v_cache + src * block_vecs;
     u32x4* kd = k_cache + dst * block_vecs;
     u32x4* vd = v_cache + dst * block_vecs;
+    constexpr int kPerThread = kVecsPerWg / kThreads;
+    if (hi - lo == kVecsPerWg) {  // a whole chunk: all loads in flight before the stores
+        u32x4 a[kPerThread], b[kPerThread];
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int64_t i = lo + threadIdx.x + (int64_t)j * kThreads;
+            a[j] = __builtin_nontemporal_load(ks + i);
+            b[j] = __builtin_nontemporal_load(vs + i);
+        }
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int64_t i = lo + threadIdx.x + (int64_t)j * kThreads;
+            kd[i] = a[j];
+            vd[i] = b[j];
+        }
+        return;
+    }
     for (int64_t i = lo + threadIdx.x; i < hi; i += kThreads) {
-        const u32x4 a = ks[i];
-        const u32x4 b = vs[i];
+        const u32x4 a = __builtin_nontemporal_load(ks + i);
+        const u32x4 b = __builtin_nontemporal_load(vs + i);
         kd[i] = a;
         vd[i] = b;
     }
