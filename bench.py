@@ -69,13 +69,21 @@ def _args():
     return ap.parse_args()
 
 
-def _sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def _code_sha(path):
+    """sha256 (16 hex digits) of a C/HIP source with its comments and blank
+    lines removed: a comment edit does not invalidate counters taken on the
+    same code."""
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def _traffic(config_name):
     """Per-launch HBM bytes from committed counter runs, if they were taken
-    on the current kernel source; else None."""
+    on the current kernel code (comments aside); else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -84,7 +92,7 @@ def _traffic(config_name):
     except (ValueError, AttributeError):
         return None
     src = os.path.join(ROOT, "paged_kv_cache_155_amd", "csrc", "pa_decode.hip")
-    if not rec or rec.get("kernel_source_sha") != _sha(src):
+    if not rec or rec.get("kernel_code_sha") != _code_sha(src):
         return None
     return rec.get("bytes_per_launch")
 

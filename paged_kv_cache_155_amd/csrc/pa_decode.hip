@@ -41,8 +41,10 @@
 //   * base-2 exponent: logits are scaled by scale*log2(e) (times the K scale
 //     for FP8) and exponentiated with v_exp_f32;
 //   * split context: each partition writes (m, l, normalised row) to the
-//     workspace; pa_reduce merges them with the log-sum-exp identity.
-//     A single-partition (sequence, head) writes its fp16 row directly.
+//     workspace; the reduce kernel merges them with the log-sum-exp identity.
+//     A single-partition (sequence, head) writes its fp16 row directly - or,
+//     behind a shared prefix whose pieces already sit in the first workspace
+//     slots, merges those slots itself and writes the row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
