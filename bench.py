@@ -69,19 +69,28 @@ def _args():
     return ap.parse_args()
 
 
-def _code_sha(path):
-    """sha256 (16 hex digits) of a C/HIP source with its comments and blank
+def _code_sha(*paths):
+    """sha256 (16 hex digits) of C/HIP sources with their comments and blank
     lines removed: a comment edit does not invalidate counters taken on the
     same code."""
     import re
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
-    code = "\n".join(ln for ln in lines if ln.strip())
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+    parts = []
+    for path in paths:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+        parts.append("\n".join(ln for ln in lines if ln.strip()))
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()[:16]
 
 
-def _traffic(config_name):
+CSRC = os.path.join(ROOT, "paged_kv_cache_155_amd", "csrc")
+# sources whose code the counters of each kind of call were taken on
+TRAFFIC_SOURCES = {"decode": ("pa_decode.hip",),
+                   "cascade": ("pa_decode.hip", "pa_multiquery.hip"),
+                   "multi_query": ("pa_multiquery.hip",)}
+
+
+def _traffic(config_name, kind="decode"):
     """Per-launch HBM bytes from committed counter runs, if they were taken
     on the current kernel code (comments aside); else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -91,8 +100,8 @@ def _traffic(config_name):
         rec = json.load(open(path)).get(config_name)
     except (ValueError, AttributeError):
         return None
-    src = os.path.join(ROOT, "paged_kv_cache_155_amd", "csrc", "pa_decode.hip")
-    if not rec or rec.get("kernel_code_sha") != _code_sha(src):
+    srcs = [os.path.join(CSRC, f) for f in TRAFFIC_SOURCES[kind]]
+    if not rec or rec.get("kernel_code_sha") != _code_sha(*srcs):
         return None
     return rec.get("bytes_per_launch")
 
@@ -136,7 +145,7 @@ def _time_events(fn, iters, warmup=3):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def bench_blocks(op, pairs, iters):
+def bench_blocks(op, pairs, iters, cpu=None):
     """copy_blocks: `pairs` random (src -> fresh dst) block copies inside
     config 1's K/V pool; swap: `pairs` blocks of K and of V out to pinned host
     memory and back in.  One JSON line per measured direction."""
@@ -157,11 +166,24 @@ def bench_blocks(op, pairs, iters):
         ms = _time_events(lambda: pa.copy_blocks(kc, vc, mapping), iters)
         moved = n * block_bytes * 2 * 2  # K and V, read + write
         t = float(np.median(ms)) * 1e-3
+        line_cpu = None
+        if cpu is not None:  # the oracle's block copy on host copies of the same pool
+            import oracle
+            orc = oracle.get()
+            okc, ovc = w.k_cache.copy(), w.v_cache.copy()
+            m = mapping.cpu().numpy()
+            dt, runs = _time_oracle(lambda: orc.copy_blocks(okc, ovc, m), cpu.cpu_repeats,
+                                    cpu.cpu_seconds / 4)
+            line_cpu = {"value": round(moved / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                        "kind": "oracle", "cpu": _cpu_model(),
+                        "sample": f"the same {n} block pairs on host copies of the pool; "
+                                  f"median of {runs} runs = {dt * 1e3:.2f} ms"}
         lines.append({"op": "copy_blocks", "pairs": n, "block_bytes": block_bytes,
                       "bytes_per_call": moved, "us_median": round(t * 1e6, 2),
                       "roofline": {"bound": "hbm", "achieved": round(moved / t / 1e9, 1),
                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": round(moved / t / 1e9 / HBM_PEAK_GBS, 4)}})
+                                   "frac": round(moved / t / 1e9 / HBM_PEAK_GBS, 4)},
+                      "cpu_baseline": line_cpu})
     else:
         hk = torch.empty((n,) + tuple(kc.shape[1:]), dtype=torch.float16).pin_memory()
         hv = torch.empty_like(hk).pin_memory()
@@ -176,15 +198,35 @@ def bench_blocks(op, pairs, iters):
             pa.swap_blocks(hk, kc, in_map)
             pa.swap_blocks(hv, vc, in_map)
 
+        orc = None
+        if cpu is not None:  # the oracle's block swap between host arrays of the same shapes
+            import oracle
+            orc = oracle.get()
+            hpool_k, hpool_v = w.k_cache.copy(), w.v_cache.copy()
+            hbuf_k = np.zeros((n,) + w.k_cache.shape[1:], dtype=np.float16)
+            hbuf_v = np.zeros_like(hbuf_k)
+            om, im = out_map.numpy(), in_map.numpy()
+            oracle_fns = {"swap_out": lambda: (orc.swap_blocks(hpool_k, hbuf_k, om),
+                                               orc.swap_blocks(hpool_v, hbuf_v, om)),
+                          "swap_in": lambda: (orc.swap_blocks(hbuf_k, hpool_k, im),
+                                              orc.swap_blocks(hbuf_v, hpool_v, im))}
         for name, fn in (("swap_out", out_), ("swap_in", in_)):
             ms = _time_events(fn, iters)
             moved = n * block_bytes * 2
             t = float(np.median(ms)) * 1e-3
+            line_cpu = None
+            if orc is not None:
+                dt, runs = _time_oracle(oracle_fns[name], cpu.cpu_repeats, cpu.cpu_seconds / 4)
+                line_cpu = {"value": round(moved / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                            "kind": "oracle", "cpu": _cpu_model(),
+                            "sample": f"the same {n} blocks of K and of V between host arrays; "
+                                      f"median of {runs} runs = {dt * 1e3:.2f} ms"}
             lines.append({"op": name, "pairs": n, "block_bytes": block_bytes,
                           "bytes_per_call": moved, "us_median": round(t * 1e6, 2),
                           "roofline": {"bound": "pcie", "achieved": round(moved / t / 1e9, 2),
                                        "peak": PCIE5_X16_GBS, "unit": "GB/s",
-                                       "frac": round(moved / t / 1e9 / PCIE5_X16_GBS, 4)}})
+                                       "frac": round(moved / t / 1e9 / PCIE5_X16_GBS, 4)},
+                          "cpu_baseline": line_cpu})
     for ln in lines:
         print(json.dumps(ln), flush=True)
 
@@ -254,7 +296,8 @@ def bench_cascade(iters, warmup, cpu=None):
         "roofline": {"bound": "hbm", "achieved": round(uniq / (dec * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(uniq / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "bytes": "unique K/V bytes"},
+                     "bytes": "unique K/V bytes",
+                     "traffic": _traffic("cascade_config3_B16_P0", "cascade")},
         "logical_kv_gbs": round(logical / (dec * 1e-3) / 1e9, 1),
         "cpu_baseline": line_cpu}), flush=True)
 
@@ -303,7 +346,8 @@ def bench_multi_query(iters, warmup, cpu=None):
         "query_tokens_per_s": round(S * n / t, 1),
         "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 2),
                      "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flops / t / 1e12 / MFMA_F16_TFLOPS, 4)},
+                     "frac": round(flops / t / 1e12 / MFMA_F16_TFLOPS, 4),
+                     "traffic": _traffic("multi_query_16x2048_last512", "multi_query")},
         "kv_unique_gbs": round(kv_unique / t / 1e9, 1), "cpu_baseline": line_cpu}), flush=True)
 
 
@@ -352,7 +396,7 @@ def _time_oracle(fn, repeats, seconds):
     return float(np.median(times)), len(times)
 
 
-def cpu_baseline(w, sample_tokens, repeats, seconds):
+def cpu_baseline(w, sample_tokens, repeats, seconds, f8=None):
     """Time the oracle (as it stands) on a bounded, deterministic sample of
     (sequence, head) pairs of the same workload (the whole workload when it
     is under the cap); GB/s over the sampled K/V bytes, median of the runs
@@ -361,8 +405,19 @@ def cpu_baseline(w, sample_tokens, repeats, seconds):
     import oracle
     from paged_kv_cache_155_amd.workloads import kv_bytes_per_token
     orc = oracle.get()
-    kc, vc = w.k_cache.copy(), w.v_cache.copy()
-    orc.reshape_and_cache(w.key, w.value, kc, vc, w.slot_mapping)
+    if f8 is None:
+        kc, vc = w.k_cache.copy(), w.v_cache.copy()
+        orc.reshape_and_cache(w.key, w.value, kc, vc, w.slot_mapping)
+
+        def run(pairs):
+            orc.decode_pairs(pairs, w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale))
+    else:  # the FP8 caches as the GPU holds them, the oracle's FP8 decode
+        kc, vc = f8.k_cache.copy(), f8.v_cache.copy()
+        orc.reshape_and_cache_fp8(w.key, w.value, kc, vc, w.slot_mapping, f8.k_scale, f8.v_scale)
+
+        def run(pairs):
+            orc.decode_fp8(w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale),
+                           f8.k_scale, f8.v_scale, pairs=pairs)
     S, H = w.num_seqs, w.num_heads
     pairs = [(s, h) for s in range(S) for h in range(H)]
     rng = np.random.default_rng(155)
@@ -374,27 +429,24 @@ def cpu_baseline(w, sample_tokens, repeats, seconds):
         s, h = pairs[i]
         chosen.append((s, h))
         tok += int(w.context_lens[s])
-    dt, runs = _time_oracle(lambda: orc.decode_pairs(chosen, w.q, kc, vc, w.block_tables,
-                                                      w.context_lens, float(w.scale)),
-                            repeats, seconds)
+    dt, runs = _time_oracle(lambda: run(chosen), repeats, seconds)
     threads = orc.threads_used
     # one core, on every 16th pair of the same sample
     one = chosen[::16]
     one_tok = sum(int(w.context_lens[s]) for s, _ in one)
     orc.set_threads(1)
     try:
-        dt1, runs1 = _time_oracle(lambda: orc.decode_pairs(one, w.q, kc, vc, w.block_tables,
-                                                            w.context_lens, float(w.scale)),
-                                  repeats, seconds / 4)
+        dt1, runs1 = _time_oracle(lambda: run(one), repeats, seconds / 4)
     finally:
         orc.set_threads(0)
-    nbytes = tok * kv_bytes_per_token(1, w.head_dim)
-    one_bytes = one_tok * kv_bytes_per_token(1, w.head_dim)
+    nbytes = tok * kv_bytes_per_token(1, w.head_dim) // (2 if f8 is not None else 1)
+    one_bytes = one_tok * kv_bytes_per_token(1, w.head_dim) // (2 if f8 is not None else 1)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "value_1core": round(one_bytes / dt1 / 1e9, 4),
             "cpu": _cpu_model(),
             "sample": f"{len(chosen)} of {len(pairs)} (sequence, head) pairs (seeded permutation), "
-                      f"{tok} token-heads = {nbytes} K/V bytes; fp64 oracle decode, median of "
+                      f"{tok} token-heads = {nbytes} K/V bytes; fp64 oracle "
+                      f"{'FP8 ' if f8 is not None else ''}decode, median of "
                       f"{runs} runs = {dt:.3f} s wall on {threads} threads; "
                       f"value_1core: every 16th of those pairs on 1 thread, median of {runs1} "
                       f"runs = {dt1:.3f} s; "
@@ -430,7 +482,7 @@ def main():
         bench_multi_query(a.steps, a.warmup, None if a.no_cpu_baseline else a)
         return
     if a.op != "step":
-        bench_blocks(a.op, a.pairs, a.steps)
+        bench_blocks(a.op, a.pairs, a.steps, None if a.no_cpu_baseline else a)
         return
 
     w = make_workload(a.config, block_size=a.block_size, partition_size=a.partition_size,
@@ -533,13 +585,14 @@ def main():
                      "measured_peak": _measured_peak(),
                      "frac_of_measured": (round(achieved / _measured_peak(), 4)
                                           if _measured_peak() else None),
-                     "traffic": None if fp8 else _traffic(f"config{a.config}_B{w.block_size}_P{P}"),
+                     "traffic": _traffic(("fp8_" if fp8 else "") + f"config{a.config}_B{w.block_size}_P{P}"),
                      "kernel": ("pa_decode_fp8" if fp8 else "pa_decode")
                                + " (partition kernel + reduce kernel), HIP events"},
         "cpu_baseline": None,
     }
-    if not a.no_cpu_baseline and not fp8:
-        line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens, a.cpu_repeats, a.cpu_seconds)
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens, a.cpu_repeats, a.cpu_seconds,
+                                            f8 if fp8 else None)
     print(json.dumps(line), flush=True)
 
 
