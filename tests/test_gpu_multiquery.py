@@ -95,9 +95,11 @@ def test_cascade_matches_plain_decode(orc, kw, P):
     log(f"[cascade] max abs err {ea:.3e}")
 
 
-@pytest.mark.parametrize("prefix_blocks,B", [(4, 16), (9, 16), (5, 32)],
-                         ids=["prefix64_B16", "prefix144_B16", "prefix160_B32"])
-def test_cascade_suffix_edges(orc, prefix_blocks, B):
+@pytest.mark.parametrize("prefix_blocks,B,D", [(4, 16, 128), (9, 16, 128), (5, 32, 128),
+                                                (9, 16, 64), (5, 32, 64)],
+                         ids=["prefix64_B16", "prefix144_B16", "prefix160_B32",
+                              "prefix144_B16_D64", "prefix160_B32_D64"])
+def test_cascade_suffix_edges(orc, prefix_blocks, B, D):
     """Suffixes of length 0 (the whole context is the prefix), 1, and a
     block and a partition boundary; a batch size that is not a multiple of 16;
     prefixes that end inside a 64-token chunk and inside a prefix partition.
@@ -106,22 +108,22 @@ def test_cascade_suffix_edges(orc, prefix_blocks, B):
     import torch
     import paged_kv_cache_155_amd as pa
     from paged_kv_cache_155_amd.workloads import make_random
-    log(f"[cascade] suffix edges prefix {prefix_blocks} blocks of {B}")
+    log(f"[cascade] suffix edges prefix {prefix_blocks} blocks of {B}, head_dim {D}")
     suffix = [0, 1, 15, 16, 17, 511, 512, 513, 0, 40, 3, 100, 64, 65, 2, 1, 0, 300]
     S = len(suffix)
     plen = prefix_blocks * B
-    w = make_random([plen + x for x in suffix], 2, 128, B, seed=41 + B, poison=True)
+    w = make_random([plen + x for x in suffix], 2, D, B, seed=41 + B + D, poison=True)
     w.block_tables[:, :prefix_blocks] = w.block_tables[0, :prefix_blocks]
     kc, vc = w.k_cache.copy(), w.v_cache.copy()
     ok = w.slot_mapping >= 0
-    kc.reshape(-1, 2, 128)[w.slot_mapping[ok]] = np.float16(0.1)   # no new token here
-    vc.reshape(-1, 2, 128)[w.slot_mapping[ok]] = np.float16(0.2)
+    kc.reshape(-1, 2, D)[w.slot_mapping[ok]] = np.float16(0.1)   # no new token here
+    vc.reshape(-1, 2, D)[w.slot_mapping[ok]] = np.float16(0.2)
     ref = orc.decode(w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale))
     prefix = w.block_tables[0, :prefix_blocks].astype(np.int32)
     st = np.ascontiguousarray(w.block_tables[:, prefix_blocks:])
     sl = np.array(suffix, dtype=np.int32)
     for P in (0, B, 512):
-        out = to_dev(np.full((S, 2, 128), np.nan, dtype=np.float16))
+        out = to_dev(np.full((S, 2, D), np.nan, dtype=np.float16))
         pa.decode_cascade(out, to_dev(w.q), to_dev(kc), to_dev(vc), to_dev(prefix),
                           plen, to_dev(st), to_dev(sl), float(w.scale), partition_size=P)
         torch.cuda.synchronize()
