@@ -376,6 +376,13 @@ def _measured_peak():
         return None
 
 
+def _device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1)}
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -592,10 +599,13 @@ def main():
             "decode_only_tokens_per_s_per_layer": round(w.num_seqs / (t_dec * 1e-3), 1),
             "t_decode_us_mean": round(t_dec * 1e3, 2),
             "t_decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
+            "t_decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                                    round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
             "t_reshape_us_mean": round(t_rc * 1e3, 2),
             "t_step_instrumented_us_mean": round(float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
                                                  * 1e3, 2),
             "wall_s_timed": round(wall, 4), "accumulate": "f32", "flush": bool(a.flush),
+            "device": _device_info(torch),
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
