@@ -186,16 +186,26 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     }
 
     // ---- loader role: 4 tokens (4*lq .. 4*lq+3 of the chunk) x dims 8*lp .. 8*lp+7 ----
-    const bool loader = tid < UNITS;
+    const bool loader = UNITS == kMqThreads || tid < UNITS;  // a constant when all threads load
     const int lp = tid % DG, lq = tid / DG;
     const int64_t block_elems = (int64_t)B * P.num_heads * D;
     const int token_stride = P.num_heads * D;
     u32x4 kr[4], vr[4];
-    auto load_chunk = [&](int t0) {
+    // The physical block of this thread's four tokens of the chunk at t0 (one
+    // block, as 4 divides B).  Loaded a chunk ahead of its K/V loads, so that
+    // their addresses never wait on a table read.  The position is clamped
+    // into the stream (the entry is then unused), so the read is always inside
+    // the table and needs no select: a select would make the compiler drain
+    // the loads in flight before overwriting the register.
+    auto chunk_block = [&](int t0) {
+        const int t = max(0, min(t0 + 4 * lq, stream_end - 1));
+        return table[t / B];
+    };
+    auto load_chunk = [&](int t0, int blk) {
         const int t = t0 + 4 * lq;
         if (!loader)
             return;  // (only when D < 128: these threads stage nothing)
-        const int64_t base = t < stream_end ? (int64_t)table[t / B] * block_elems +
+        const int64_t base = t < stream_end ? (int64_t)blk * block_elems +
                                                   (int64_t)(t % B) * token_stride + h * D + 8 * lp
                                             : 0;
         if (t + 4 <= stream_end) {  // all four tokens exist: no selects
@@ -216,7 +226,16 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
         }
     };
 
-    load_chunk(stream_begin);
+    load_chunk(stream_begin, chunk_block(stream_begin));
+    int next_blk = chunk_block(stream_begin + N);
+    // Wait for q here, once: inside the loop the compiler cannot prove these
+    // loads complete on every path and would otherwise drain every load in
+    // flight (the next chunk's prefetch included) before the first product.
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int i = 0; i < KI; ++i)
+            asm volatile("" ::"v"(qf[qt][i]));
     int buf = 0;
     for (int t0 = stream_begin; t0 < stream_end; t0 += N, buf ^= 1) {
         _Float16* ks = k_lds[buf];
@@ -229,7 +248,8 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
             }
         }
         if (t0 + N < stream_end)
-            load_chunk(t0 + N);  // in flight during this chunk's math
+            load_chunk(t0 + N, next_blk);  // in flight during this chunk's math
+        next_blk = chunk_block(t0 + 2 * N);  // unconditional, so no copy waits on it
         __syncthreads();
 
         if (wrows > 0 && t0 < wave_hi) {  // wave-uniform: some row of this wave sees the chunk
