@@ -200,6 +200,11 @@ __device__ __forceinline__ void tile_step(LaneState<KV>& st, const TileCtx<KV>& 
             vr[j] = u32x4{0, 0, 0, 0};
         }
     }
+    // FP8: all 2 * kLoads loads issued before any arithmetic (the scheduler otherwise starts the
+    // K dot products as the first loads land, keeping about half of them in flight); measured
+    // 1-2% faster for FP8 and 1% slower for fp16, which keeps the default schedule.
+    if constexpr (KV::kElemBytes == 1)
+        __builtin_amdgcn_sched_barrier(0);
     float x[kLoads];
     float tmax = kNegInf;
 #pragma unroll
