@@ -130,9 +130,13 @@ hipError_t enqueue_swap_blocks(const void* src, void* dst, const int64_t* block_
 {
     void* src_dev = reachable(src);
     void* dst_dev = reachable(dst);
+    // (the kernel path also needs its grid, kPairsPerLaunch blocks of
+    // ceil(block_vecs / kVecsPerWg) workgroups, to stay under 2^32 work-items)
     if (src_dev && dst_dev && block_bytes % 16 == 0 &&
         (reinterpret_cast<uintptr_t>(src_dev) & 15u) == 0 &&
-        (reinterpret_cast<uintptr_t>(dst_dev) & 15u) == 0) {
+        (reinterpret_cast<uintptr_t>(dst_dev) & 15u) == 0 &&
+        (block_bytes / 16 + kVecsPerWg - 1) / kVecsPerWg * kPairsPerLaunch <=
+            (int64_t)(UINT32_MAX / kThreads)) {
         const int64_t block_vecs = block_bytes / 16;
         const int32_t chunks = (int32_t)((block_vecs + kVecsPerWg - 1) / kVecsPerWg);
         for (int32_t i0 = 0; i0 < num_pairs; i0 += kPairsPerLaunch) {

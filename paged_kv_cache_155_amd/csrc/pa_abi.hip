@@ -13,6 +13,10 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A launch is at most 2^32 - 1 work-items: a grid of `workgroups` workgroups
+// of 256 threads fits.
+bool grid_fits(int64_t workgroups) { return workgroups <= (int64_t)(UINT32_MAX / 256); }
+
 // Number of context partitions the grid covers, or -1 for bad arguments.
 int64_t num_partitions(int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size)
 {
@@ -76,6 +80,8 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
         return PA_ERR_INVALID_DIM;
     if (num_tokens == 0)
         return PA_OK;
+    if (!grid_fits(num_tokens))  // one workgroup per token
+        return PA_ERR_INVALID_DIM;
     if (!key || !value || !k_cache || !v_cache || !slot_mapping)
         return PA_ERR_NULL;
     if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
@@ -140,6 +146,8 @@ int prepare_decode(pa::DecodeParams& p, void* out, const void* q, const void* k_
     const int64_t units = (int64_t)num_seqs * num_heads * np;
     const int64_t slots = np + extra_slots;
     if (units > INT32_MAX || (int64_t)num_seqs * num_heads * slots > INT32_MAX)
+        return PA_ERR_INVALID_DIM;
+    if (!grid_fits(units))
         return PA_ERR_INVALID_DIM;
 
     p = pa::DecodeParams{};
@@ -226,7 +234,7 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
     if (!prefix_block_table)
         return PA_ERR_NULL;
     const int64_t row_tiles = ((int64_t)num_seqs + pa::kCascadeTileRows - 1) / pa::kCascadeTileRows;
-    if (row_tiles * num_heads * parts > INT32_MAX)
+    if (row_tiles * num_heads * parts > INT32_MAX || !grid_fits(row_tiles * num_heads * parts))
         return PA_ERR_INVALID_DIM;
     pa::MqParams m{};
     m.ws_o = p.ws_o;
@@ -280,7 +288,7 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
         return PA_ERR_ALIGN;
     const int64_t tiles = ((int64_t)max_query_len + pa::kMqTileRows - 1) / pa::kMqTileRows;
     const int64_t units = (int64_t)num_seqs * tiles * num_heads;
-    if (units > INT32_MAX)
+    if (units > INT32_MAX || !grid_fits(units))
         return PA_ERR_INVALID_DIM;
     pa::MqParams m{};
     m.out = static_cast<_Float16*>(out);
@@ -354,6 +362,8 @@ int pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, 
         return PA_ERR_INVALID_DIM;
     if (num_tokens == 0)
         return PA_OK;
+    if (!grid_fits(num_tokens))  // one workgroup per token
+        return PA_ERR_INVALID_DIM;
     if (!key || !value || !k_cache || !v_cache || !slot_mapping)
         return PA_ERR_NULL;
     if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
@@ -387,7 +397,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
         return PA_ERR_ALIGN;
     const int64_t block_vecs = (int64_t)block_size * num_heads * head_dim / 8;
     const int64_t chunks = (block_vecs + 2047) / 2048;
-    if ((int64_t)num_pairs * chunks > INT32_MAX)
+    if ((int64_t)num_pairs * chunks > INT32_MAX || !grid_fits((int64_t)num_pairs * chunks))
         return PA_ERR_INVALID_DIM;
     hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_blocks,
                                           block_vecs, static_cast<hipStream_t>(stream));

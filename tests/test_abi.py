@@ -76,6 +76,8 @@ def test_decode_rejects(lib):
     assert _decode(lib, q=P(0x10008)) == -6
     assert _decode(lib, scale=float("nan")) == -2
     assert _decode(lib, S=0, out=P(0)) == 0          # nothing to do
+    # 65536 x 256 workgroups of 256 threads would pass 2^32 work-items
+    assert _decode(lib, S=65536, H=256) == -2
 
 
 def test_reshape_rejects(lib):
@@ -85,6 +87,7 @@ def test_reshape_rejects(lib):
     assert f(FAKE, P(0), FAKE, FAKE, FAKE, 3, 4, 128, 8, 16, None) == -1
     assert f(FAKE, FAKE, P(0x10004), FAKE, FAKE, 3, 4, 128, 8, 16, None) == -6
     assert f(P(0), P(0), P(0), P(0), P(0), 0, 4, 128, 8, 16, None) == 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 24, 4, 128, 8, 16, None) == -2  # grid too large
 
 
 def test_copy_and_swap_reject(lib):
