@@ -198,3 +198,75 @@ def test_error_paths_enqueue_nothing():
     assert e.value.code == -4
     torch.cuda.synchronize()
     assert torch.isnan(d.out.float()).all(), "a rejected call wrote output"
+
+
+def test_graph_capture_replays_match_eager(orc):
+    """The library enqueues only kernels (no allocation, memset or host
+    sync), so a step can be captured in a HIP graph: reshape_and_cache +
+    the split decode (P = 512, reduce included) captured once and replayed
+    three times, with eager work and synchronisations between replays; every
+    replay is bitwise equal to the eager step and within the tolerance of
+    the oracle."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import make_workload
+    w = make_workload(1, num_seqs=16, num_heads=8)
+    log(f"[edge] graph capture S={w.num_seqs} H={w.num_heads} P=512")
+    d = DeviceWorkload(w)
+    ws = torch.empty(max(16, pa.decode_workspace_size(w.num_seqs, w.num_heads, w.head_dim,
+                                                      w.block_size, w.max_blocks_per_seq, 512)),
+                     dtype=torch.uint8, device="cuda")
+    eager = torch.full_like(d.q, float("nan"))
+    d.reshape_and_cache()
+    d.decode(512, out=eager, workspace=ws)
+    torch.cuda.synchronize()
+    _, _, ref = oracle_after_write(orc, w)
+    assert_close(eager.cpu().numpy(), ref, "eager step before capture")
+    out = torch.full_like(d.q, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            d.reshape_and_cache()
+            d.decode(512, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(0xFF)  # the replay must not rely on what the workspace held
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.uint16), eager.cpu().numpy().view(np.uint16)), \
+            f"replay {i} differs from the eager step"
+
+
+def test_concurrent_streams(orc):
+    """Two decodes with their own outputs and workspaces on two streams at
+    once (both at the default priority) give the same bits as one at a time."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import make_workload
+    log("[edge] two streams")
+    ws_, outs, seq = [], [], []
+    works = [DeviceWorkload(make_workload(1, num_seqs=24, num_heads=8, variant=v)) for v in (1, 2)]
+    for d in works:
+        d.reshape_and_cache()
+        w = d.w
+        ws_.append(torch.empty(max(16, pa.decode_workspace_size(
+            w.num_seqs, w.num_heads, w.head_dim, w.block_size, w.max_blocks_per_seq, 512)),
+            dtype=torch.uint8, device="cuda"))
+        seq.append(d.decode(512, out=torch.empty_like(d.q), workspace=ws_[-1]).clone())
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        for d, ws, st in zip(works, ws_, streams):
+            with torch.cuda.stream(st):
+                outs.append(d.decode(512, out=torch.empty_like(d.q), workspace=ws))
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int16), seq[i % 2].view(torch.int16)), f"call {i}"
