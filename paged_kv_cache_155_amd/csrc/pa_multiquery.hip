@@ -32,8 +32,9 @@
 //       online softmax   per query column (lane = query, 16 tokens per lane),
 //                        base-2 exponent; the running max is exchanged across
 //                        the four lane groups with permlane swaps, the running
-//                        sum stays per lane until the end; O is rescaled only
-//                        when some row's max moved
+//                        sum stays per lane until the end; the reference max
+//                        moves, and O is rescaled, only when some row's chunk
+//                        max passes it by more than 2^8 (lazy rescaling)
 //       O^T += V^T P^T   v_mfma_f32_16x16x32_f16 over 32 tokens; the S^T
 //                        tiles are already P^T in the B-operand layout, and
 //                        the V^T operand comes from the transposing LDS read
@@ -54,6 +55,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = kMqThreads / kWave;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLazyRescale = 8.0f;  // log2 units: weights stay below 256
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -299,11 +301,18 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         bmax = fmaxf(bmax, st[qt][s][j]);
-                // scale > 0, so the max of the raw scores gives the max of the scaled ones
-                const float m_new = fmaxf(m[qt], group_max(bmax) * P.scale_log2);
+                // scale > 0, so the max of the raw scores gives the max of the scaled ones.
+                // m is the reference the exponentials are taken against, moved (and O, l
+                // rescaled) only when a chunk's max passes it by more than kLazyRescale:
+                // the weights then stay below 2^kLazyRescale, far inside fp16 and fp32,
+                // and the rescale of O is skipped in most chunks (the result is the same
+                // softmax: O and l share the reference).
+                const float cm = group_max(bmax) * P.scale_log2;
+                const bool up = cm > m[qt] + kLazyRescale;  // any finite cm while m = -inf
+                const float m_new = up ? cm : m[qt];
                 const float m_ref = m_new == kNegInf ? 0.0f : m_new;
-                alpha[qt] = exp2_fast(m[qt] - m_ref);
-                moved |= m_new != m[qt];
+                alpha[qt] = up ? exp2_fast(m[qt] - m_ref) : 1.0f;
+                moved |= up;
                 m[qt] = m_new;
                 float psum = 0.0f;
 #pragma unroll
