@@ -44,7 +44,8 @@ def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first (the GPU's clocks settle within some 20 ms)")
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
@@ -341,8 +342,9 @@ def bench_multi_query(iters, warmup, cpu=None):
     bt, cl, qst = up(w.block_tables), up(w.context_lens), up(qs)
     out = torch.empty_like(q)
     scale = float(w.scale)
+    # at least 100 untimed calls (~35 ms): the matrix-core clock settles over the first ~20 ms
     ms = _time_events(lambda: pa.multi_query(out, q, kc, vc, bt, cl, qst, n, scale), iters,
-                      warmup)
+                      max(warmup, 100))
     t = float(np.median(ms)) * 1e-3
     H, D = w.num_heads, w.head_dim
     visible = sum(ctx - n + i + 1 for i in range(n)) * S          # (row, key) pairs per head
