@@ -270,3 +270,19 @@ def test_concurrent_streams(orc):
     torch.cuda.synchronize()
     for i, o in enumerate(outs):
         assert torch.equal(o.view(torch.int16), seq[i % 2].view(torch.int16)), f"call {i}"
+
+
+@pytest.mark.parametrize("S,H,D,B,lens,P", [
+    (3, 5, 64, 32, [1, 777, 4100], 64),         # odd head count, long tail past a partition
+    (3, 5, 64, 32, [1, 777, 4100], 0),
+    (1, 1, 128, 16, [65536], 512),              # one long sequence: 128 partitions, one head
+    (9, 12, 128, 16, [3000, 1, 0, 17, 2048, 2049, 511, 513, 4095], 2048),
+], ids=["H5_D64_B32_P64", "H5_D64_B32_P0", "S1_H1_64K_P512", "H12_mixed_P2048"])
+def test_odd_shapes(orc, S, H, D, B, lens, P):
+    """Shapes no config uses: head counts that are not a multiple of the
+    XCD count, a single 64K-token sequence with one head, a batch of mixed
+    lengths including 0 and 1 with a large partition."""
+    from paged_kv_cache_155_amd.workloads import make_random
+    log(f"[edge] odd shape S={S} H={H} D={D} B={B} P={P} lens={lens}")
+    w = make_random(lens, H, D, B, seed=S * 100 + H + D + B + P, partition_size=P)
+    _parity(orc, w, P, f"odd shape S={S} H={H} D={D} B={B} P={P}")
