@@ -171,6 +171,40 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step of a shared-prefix batch in one call: pa_reshape_and_cache
+ * of this step's tokens followed by pa_decode_cascade ([10x] §2.3: each new
+ * token's K/V go into the slot its block table names, then attention runs
+ * over the context that now includes it).  Token s of key / value is the new
+ * token of sequence s; it belongs to the private suffix.
+ *
+ *   key, value     fp16 [num_seqs, num_heads, head_dim] (read)
+ *   k_cache,
+ *   v_cache        as pa_decode_cascade, and written: row s of key / value
+ *                  goes to slot_mapping[s] exactly as pa_reshape_and_cache
+ *                  puts it (bit patterns kept; slots outside [0, num_blocks *
+ *                  block_size) skipped)
+ *   slot_mapping   int64 [num_seqs], DEVICE, 8-byte aligned
+ * Other arguments, workspace and errors as pa_decode_cascade; key / value
+ * 16-byte aligned.
+ *
+ * The writes are made by the prefix pass, which reads only the prefix blocks,
+ * and the suffix partitions run after it on the stream, so no second launch
+ * is needed.  Precondition: no slot_mapping[s] lies in a prefix block (a new
+ * token always lands in a private block; [arch] §2.3: a shared block is
+ * copied before a sequence writes into it).  Then out and both caches are
+ * bitwise what pa_reshape_and_cache (num_tokens = num_seqs) followed by
+ * pa_decode_cascade produce.  prefix_len = 0 runs exactly those two steps.
+ */
+int pa_decode_cascade_append(void* out, const void* q, const void* key, const void* value,
+                             void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                             const int32_t* prefix_block_table, int32_t prefix_len,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                             int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                             float scale, int32_t partition_size, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * Multi-query paged attention: several new tokens per sequence in one batch
  * (chunked prefill, or prefill mixed with decode: [10x] §4.3, [eng] §4.2).
  * Sequence s brings n_s = query_start[s+1] - query_start[s] query rows; they

@@ -55,6 +55,9 @@ def load(path=None):
     lib.pa_decode_cascade.argtypes = ([_P] * 5 + [_I32] + [_P] * 2 + [_I32] * 6
                                       + [ctypes.c_float, _I32, _P, ctypes.c_size_t, _P])
     lib.pa_decode_cascade.restype = ctypes.c_int
+    lib.pa_decode_cascade_append.argtypes = ([_P] * 8 + [_I32] + [_P] * 2 + [_I32] * 6
+                                             + [ctypes.c_float, _I32, _P, ctypes.c_size_t, _P])
+    lib.pa_decode_cascade_append.restype = ctypes.c_int
     lib.pa_multi_query.argtypes = [_P] * 7 + [_I32] * 8 + [ctypes.c_float, _P]
     lib.pa_multi_query.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]
@@ -155,6 +158,13 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, partitio
     if rc != PA_OK:
         raise PAError(rc, "pa_decode")
     return out
+
+
+def _check_new_tokens(key, value, slot_mapping, S, H, D):
+    import torch
+    _check(key, "key", torch.float16, shape=(S, H, D))
+    _check(value, "value", torch.float16, shape=(S, H, D))
+    _check(slot_mapping, "slot_mapping", torch.int64, shape=(S,))
 
 
 def copy_blocks(k_cache, v_cache, block_mapping, stream=None):
@@ -298,6 +308,45 @@ def decode_cascade(out, q, k_cache, v_cache, prefix_table, prefix_len, block_tab
                                   _stream_ptr(stream))
     if rc != PA_OK:
         raise PAError(rc, "pa_decode_cascade")
+    return out
+
+
+def decode_cascade_append(out, q, key, value, k_cache, v_cache, slot_mapping, prefix_table,
+                          prefix_len, block_tables, context_lens, scale, partition_size=512,
+                          workspace=None, stream=None):
+    """reshape_and_cache(key, value, k_cache, v_cache, slot_mapping) followed by
+    decode_cascade(...), in the launches of decode_cascade alone: row s of key
+    / value [S, H, D] is sequence s's new token, slot_mapping [S] int64 its
+    slot in a private suffix block (negative: not written)."""
+    import torch
+    _check(k_cache, "k_cache", torch.float16, ndim=4)
+    NB, B, H, D = k_cache.shape
+    _check(v_cache, "v_cache", torch.float16, shape=k_cache.shape)
+    _check(q, "q", torch.float16, ndim=3)
+    S = q.shape[0]
+    _check(q, "q", torch.float16, shape=(S, H, D))
+    _check(out, "out", torch.float16, shape=(S, H, D))
+    _check_new_tokens(key, value, slot_mapping, S, H, D)
+    _check(prefix_table, "prefix_table", torch.int32, ndim=1)
+    if prefix_len % B or prefix_table.numel() * B < prefix_len:
+        raise ValueError("prefix_len must be a multiple of the block size covered by prefix_table")
+    _check(block_tables, "block_tables", torch.int32, ndim=2)
+    MB = block_tables.shape[1]
+    _check(block_tables, "block_tables", torch.int32, shape=(S, MB))
+    _check(context_lens, "context_lens", torch.int32, shape=(S,))
+    need = decode_cascade_workspace_size(S, H, D, B, int(prefix_len), MB, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check(workspace, "workspace", torch.uint8, ndim=1)
+    rc = load().pa_decode_cascade_append(_ptr(out), _ptr(q), _ptr(key), _ptr(value),
+                                         _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping),
+                                         _ptr(prefix_table), int(prefix_len), _ptr(block_tables),
+                                         _ptr(context_lens), S, H, D, NB, B, MB, float(scale),
+                                         int(partition_size), _ptr(workspace), workspace.numel(),
+                                         _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_decode_cascade_append")
     return out
 
 

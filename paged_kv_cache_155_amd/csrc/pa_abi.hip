@@ -207,21 +207,45 @@ size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads, int
     return layout((int64_t)num_seqs * num_heads * slots, head_dim).total;
 }
 
-int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* prefix_block_table, int32_t prefix_len,
-                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                      int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
-                      int32_t max_blocks_per_seq, float scale, int32_t partition_size,
-                      void* workspace, size_t workspace_bytes, void* stream)
+namespace {
+
+// pa_decode_cascade, and pa_decode_cascade_append when key != nullptr
+int cascade(void* out, const void* q, const void* key, const void* value, void* k_cache,
+            void* v_cache, const int64_t* slot_mapping, const int32_t* prefix_block_table,
+            int32_t prefix_len, const int32_t* block_tables, const int32_t* context_lens,
+            int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+            int32_t block_size, int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+            void* workspace, size_t workspace_bytes, void* stream, bool append)
 {
     if (prefix_len < 0 || (block_size > 0 && prefix_len % block_size != 0))
         return PA_ERR_INVALID_DIM;
     if (!(std::isfinite(scale) && scale > 0.0f))
         return PA_ERR_INVALID_DIM;
-    if (prefix_len == 0)  // nothing shared: the plain decode
-        return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
-                         num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq, scale,
-                         partition_size, workspace, workspace_bytes, stream);
+    if (append && (!key || !value || !slot_mapping) && num_seqs > 0)
+        return PA_ERR_NULL;
+    if (append && num_seqs > 0 &&
+        (!aligned16(key) || !aligned16(value) || (reinterpret_cast<uintptr_t>(slot_mapping) & 7u)))
+        return PA_ERR_ALIGN;
+    if (prefix_len == 0) {  // nothing shared: the plain step (its own write, then pa_decode)
+        if (!append)
+            return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                             num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
+                             scale, partition_size, workspace, workspace_bytes, stream);
+        pa::DecodeParams p;  // every decode check before the write is enqueued
+        int rc = prepare_decode(p, out, q, k_cache, v_cache, block_tables, context_lens,
+                                num_seqs, num_heads, head_dim, num_blocks, block_size,
+                                max_blocks_per_seq, scale, partition_size, workspace,
+                                workspace_bytes);
+        if (rc != PA_OK)
+            return rc == 1 ? PA_OK : rc;
+        rc = pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_seqs,
+                                  num_heads, head_dim, num_blocks, block_size, stream);
+        if (rc != PA_OK)
+            return rc;  // its checks fail before it enqueues anything
+        hipError_t e = pa::launch_decode_dispatch(p, head_dim, block_size,
+                                                  static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+    }
     if (head_dim != 64 && head_dim != 128)
         return PA_ERR_UNSUPPORTED;
     pa::DecodeParams p;
@@ -253,6 +277,18 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
     m.row_tiles = (int32_t)row_tiles;
     m.total_units = (uint32_t)(row_tiles * parts * num_heads);
     m.scale_log2 = p.scale_log2;
+    if (append) {  // the prefix pass also writes the new tokens (into private suffix slots)
+        m.new_k = static_cast<const _Float16*>(key);
+        m.new_v = static_cast<const _Float16*>(value);
+        m.k_store = static_cast<_Float16*>(k_cache);
+        m.v_store = static_cast<_Float16*>(v_cache);
+        m.slot_mapping = slot_mapping;
+        m.cache_slots = (int64_t)num_blocks * block_size;
+        const int64_t copy_units = pa::copy_workgroups(m, head_dim);
+        if (!grid_fits((int64_t)m.total_units + copy_units))
+            return PA_ERR_INVALID_DIM;
+        m.copy_units = (uint32_t)copy_units;
+    }
     // Prefix pass first (slots 0..parts-1), then the suffix partitions; when
     // every suffix fits one partition the partition kernel merges the prefix
     // slots itself and writes the rows, else the reduce merges all slots.
@@ -261,6 +297,37 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
     if (e == hipSuccess)
         e = pa::launch_decode_dispatch(p, head_dim, block_size, st);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* prefix_block_table, int32_t prefix_len,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                      int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    return cascade(out, q, nullptr, nullptr, const_cast<void*>(k_cache),
+                   const_cast<void*>(v_cache), nullptr, prefix_block_table, prefix_len,
+                   block_tables, context_lens, num_seqs, num_heads, head_dim, num_blocks,
+                   block_size, max_blocks_per_seq, scale, partition_size, workspace,
+                   workspace_bytes, stream, /*append=*/false);
+}
+
+int pa_decode_cascade_append(void* out, const void* q, const void* key, const void* value,
+                             void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                             const int32_t* prefix_block_table, int32_t prefix_len,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                             int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                             float scale, int32_t partition_size, void* workspace,
+                             size_t workspace_bytes, void* stream)
+{
+    return cascade(out, q, key, value, k_cache, v_cache, slot_mapping, prefix_block_table,
+                   prefix_len, block_tables, context_lens, num_seqs, num_heads, head_dim,
+                   num_blocks, block_size, max_blocks_per_seq, scale, partition_size, workspace,
+                   workspace_bytes, stream, /*append=*/true);
 }
 
 int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,

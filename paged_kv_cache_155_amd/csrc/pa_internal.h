@@ -58,11 +58,23 @@ struct MqParams {
     int32_t prefix_part_len;       // shared prefix: tokens per prefix partition (multiple of kMqChunk)
     int32_t prefix_parts;          // shared prefix: partitions = workspace slots 0..parts-1
     int32_t num_slots;             // shared prefix: workspace slots per (s, h)
-    uint32_t total_units;
+    uint32_t total_units;          // workgroups of query-row tiles
     float scale_log2;
+    uint32_t copy_units;           // shared prefix, appending form: copy workgroups first
+    // shared prefix, appending form (new_k == nullptr otherwise): row s of
+    // new_k / new_v [S, H, D] goes to cache slot slot_mapping[s] when
+    // 0 <= slot < cache_slots (a private suffix slot, never a prefix block)
+    const _Float16* new_k;
+    const _Float16* new_v;
+    _Float16* k_store;             // the caches again, written through these
+    _Float16* v_store;
+    const int64_t* slot_mapping;
+    int64_t cache_slots;           // num_blocks * block_size
 };
 
 hipError_t launch_multiquery(const MqParams& p, int head_dim, int block_size, hipStream_t stream);
+// extra workgroups of the appending shared-prefix pass (0 unless p.new_k)
+int64_t copy_workgroups(const MqParams& p, int head_dim);
 hipError_t launch_cascade_prefix(const MqParams& p, int head_dim, int block_size,
                                  hipStream_t stream);
 

@@ -56,6 +56,7 @@ constexpr int kWave = 64;
 constexpr int kWaves = kMqThreads / kWave;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyRescale = 8.0f;  // log2 units: weights stay below 256
+constexpr int kCopyItems = 4;         // new-row pieces per thread of a copy workgroup
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -90,6 +91,21 @@ __device__ __forceinline__ float group_sum(float x)
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+}  // namespace
+
+// Workgroups that the appending shared-prefix pass adds for the copy.
+int64_t copy_workgroups(const MqParams& P, int head_dim)
+{
+    if (P.new_k == nullptr)
+        return 0;
+    const int64_t items = (int64_t)P.num_seqs * P.num_heads * (head_dim / 8);
+    const int64_t wgs = (items + (int64_t)kMqThreads * kCopyItems - 1) /
+                        ((int64_t)kMqThreads * kCopyItems);
+    return (wgs + 7) / 8 * 8;  // whole rounds of the 8 XCDs
+}
+
+namespace {
+
 // Hardware workgroup i of n lands on XCD i % 8; XCD x gets logical range
 // [x*n/8, (x+1)*n/8).
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n)
@@ -98,6 +114,44 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n)
     const uint32_t q = n / kXcds, r = n % kXcds;
     const uint32_t xcd = i % kXcds, k = i / kXcds;
     return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
+// Appending form of the shared-prefix pass: the first workgroups of the grid
+// copy this step's new K/V rows (row s of new_k / new_v [S, H, D]) to their
+// slots, 16 bytes of K and of V per item, kCopyItems items per thread with
+// every load (slot and data alike) issued before the first store.  The slots
+// are private suffix slots, so these writes never meet the prefix units'
+// reads.
+
+template <int D>
+__device__ void copy_new_rows(const MqParams& P, uint32_t wg)
+{
+    constexpr int kPieces = D / 8;  // 16-byte pieces of a head row
+    const int64_t items = (int64_t)P.num_seqs * P.num_heads * kPieces;
+    const int64_t first = (int64_t)wg * kMqThreads * kCopyItems + threadIdx.x;
+    u32x4 kv[kCopyItems], vv[kCopyItems];
+    int64_t dst[kCopyItems];
+#pragma unroll
+    for (int j = 0; j < kCopyItems; ++j) {
+        const int64_t i = first + (int64_t)j * kMqThreads;
+        dst[j] = -1;
+        if (i < items) {
+            const int64_t row = i / kPieces;  // sequence * H + head
+            const int piece = (int)(i % kPieces);
+            const int64_t slot = P.slot_mapping[row / P.num_heads];
+            kv[j] = *reinterpret_cast<const u32x4*>(P.new_k + row * D + piece * 8);
+            vv[j] = *reinterpret_cast<const u32x4*>(P.new_v + row * D + piece * 8);
+            if (slot >= 0 && slot < P.cache_slots)
+                dst[j] = (slot * P.num_heads + row % P.num_heads) * D + piece * 8;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kCopyItems; ++j) {
+        if (dst[j] >= 0) {
+            *reinterpret_cast<u32x4*>(P.k_store + dst[j]) = kv[j];
+            *reinterpret_cast<u32x4*>(P.v_store + dst[j]) = vv[j];
+        }
+    }
 }
 
 template <int D, int B, bool kCascade, int QT>
@@ -119,13 +173,22 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][N * KS];  // [token][dim]
     __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][N * VS];  // [token][dim]
 
+    uint32_t wg = blockIdx.x;
+    if constexpr (kCascade) {
+        if (wg < P.copy_units) {  // a copy workgroup (appending form only)
+            copy_new_rows<D>(P, wg);
+            return;  // the whole workgroup, before any barrier
+        }
+        wg -= P.copy_units;  // a multiple of 8: the XCD of each prefix unit is kept
+    }
+
     const int tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
     const int g = lane / 16;  // lane group: owns dims [g*D/4, (g+1)*D/4) of K and Q
     const int c = lane % 16;  // this lane's query column of S^T (and token row of K)
 
     // ---- the tile of query rows and the token stream they share ----
-    const uint32_t logical = xcd_remap(blockIdx.x, P.total_units);
+    const uint32_t logical = xcd_remap(wg, P.total_units);
     const int tile = (int)(logical % (uint32_t)P.row_tiles);
     const uint32_t rest = logical / (uint32_t)P.row_tiles;
     int h, n_rows, stream_begin = 0, stream_end, lim0 = 0, part = 0;
@@ -395,7 +458,7 @@ template <bool kCascade>
 hipError_t launch_mq(const MqParams& P, int head_dim, int block_size, hipStream_t stream)
 {
     constexpr int QT = (kCascade ? kCascadeTileRows : kMqTileRows) / (kWaves * 16);
-    const dim3 grid(P.total_units), block(kMqThreads);
+    const dim3 grid(P.total_units + (kCascade ? P.copy_units : 0u)), block(kMqThreads);
     if (head_dim == 128 && block_size == 16)
         hipLaunchKernelGGL((pa_mq_kernel<128, 16, kCascade, QT>), grid, block, 0, stream, P);
     else if (head_dim == 128 && block_size == 32)

@@ -200,3 +200,30 @@ def test_multi_query_rejects(lib):
     assert _mq(lib, S=0, out=P(0)) == 0
     assert _mq(lib, T=0, out=P(0)) == 0
     assert _mq(lib, maxq=0, out=P(0)) == 0
+
+
+def _cascade_append(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, k=FAKE, v=FAKE, sm=FAKE, pt=FAKE, plen=64,
+             bt=FAKE, cl=FAKE, S=2, H=4, D=128, NB=8, B=16, MB=4, scale=0.088, P=0, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return lib.pa_decode_cascade_append(
+        a["out"], a["q"], a["key"], a["value"], a["k"], a["v"], a["sm"], a["pt"], a["plen"],
+        a["bt"], a["cl"], a["S"], a["H"], a["D"], a["NB"], a["B"], a["MB"], a["scale"], a["P"],
+        a["ws"], a["wsb"], None)
+
+
+def test_cascade_append_rejects(lib):
+    # every call below must fail validation (or have nothing to do): the pointers are fake
+    assert _cascade_append(lib, plen=17) == -2
+    assert _cascade_append(lib, scale=0.0) == -2
+    assert _cascade_append(lib, key=P(0)) == -1
+    assert _cascade_append(lib, sm=P(0)) == -1
+    assert _cascade_append(lib, value=P(0x10008)) == -6
+    assert _cascade_append(lib, sm=P(0x10004)) == -6
+    assert _cascade_append(lib, D=96) == -3
+    assert _cascade_append(lib, wsb=16) == -5
+    assert _cascade_append(lib, plen=0, key=P(0)) == -1  # no prefix: the plain step
+    assert _cascade_append(lib, plen=0, D=96) == -3      # (decode checks before the write)
+    assert _cascade_append(lib, plen=0, P=24) == -4
+    assert _cascade_append(lib, S=0, out=P(0), key=P(0), sm=P(0)) == 0  # nothing to do
