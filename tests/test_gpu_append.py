@@ -110,3 +110,61 @@ def test_no_prefix_is_the_plain_step(orc):
     gk, gv = _pools(d)
     assert np.array_equal(gk, kc.view(np.uint16)) and np.array_equal(gv, vc.view(np.uint16))
     assert_close(d.out.cpu().numpy(), oref, "no prefix")
+
+
+def test_graph_capture_replays_match_eager(orc):
+    """The appending step enqueues only kernels, so it can be captured in a
+    HIP graph: captured once and replayed three times, with the new tokens'
+    slots reset to NaN and the workspace filled with 0xFF before each replay
+    (eager work and synchronisations in between); every replay writes the
+    slots again and is bitwise equal to the eager call."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import make_workload, split_shared_prefix
+    w = make_workload(3, num_seqs=70, num_heads=4)
+    prefix, plen, st, sl = split_shared_prefix(w, 32)
+    log(f"[append] graph capture S={w.num_seqs} H={w.num_heads} prefix {plen}")
+    d = DeviceWorkload(w)
+    pt, stt, slt = to_dev(prefix), to_dev(st), to_dev(sl)
+    ws = torch.empty(pa.decode_cascade_workspace_size(w.num_seqs, w.num_heads, w.head_dim,
+                                                      w.block_size, plen, st.shape[1], 0),
+                     dtype=torch.uint8, device="cuda")
+    H, D = w.num_heads, w.head_dim
+
+    def step(out):
+        pa.decode_cascade_append(out, d.q, d.key, d.value, d.k_cache, d.v_cache, d.slot_mapping,
+                                 pt, plen, stt, slt, float(w.scale), partition_size=0,
+                                 workspace=ws)
+
+    def reset_slots():
+        d.k_cache.view(-1, H, D)[d.slot_mapping] = float("nan")
+        d.v_cache.view(-1, H, D)[d.slot_mapping] = float("nan")
+
+    eager = torch.full_like(d.q, float("nan"))
+    step(eager)
+    torch.cuda.synchronize()
+    kc, vc, ref = oracle_after_write(orc, w)
+    assert_close(eager.cpu().numpy(), ref, "eager step before capture")
+    pools = _pools(d)
+    assert np.array_equal(pools[0], kc.view(np.uint16))
+    out = torch.full_like(d.q, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step(out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(0xFF)
+        reset_slots()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), eager.cpu().numpy().view(np.uint16)), \
+            f"replay {i}: output differs from the eager call"
+        got = _pools(d)
+        assert np.array_equal(got[0], pools[0]) and np.array_equal(got[1], pools[1]), \
+            f"replay {i}: pools differ from the eager call"
