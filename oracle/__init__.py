@@ -69,6 +69,9 @@ class Oracle:
         lib.oracle_decode_fp8_pairs.restype = ctypes.c_int
         lib.oracle_prefill.argtypes = [_P] * 7 + [_I32] * 7 + [ctypes.c_double, _P]
         lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_prefill_fp8.argtypes = ([_P] * 7 + [_I32] * 7
+                                           + [ctypes.c_double, ctypes.c_float, ctypes.c_float, _P])
+        lib.oracle_prefill_fp8.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_set_threads.restype = ctypes.c_int
         self.lib = lib
@@ -255,6 +258,29 @@ class Oracle:
                                      float(scale), _ptr(used))
         if rc:
             raise ValueError(f"oracle_prefill failed ({rc})")
+        self.threads_used = int(used[0])
+        return out
+
+    def prefill_fp8(self, q, k_cache8, v_cache8, block_tables, context_lens, query_start, scale,
+                    k_scale, v_scale):
+        """fp64 [T, H, D]: prefill over FP8 caches (values = code * scale)."""
+        q = _u16(q)
+        T, H, D = q.shape
+        nb, bs, nh, hd = k_cache8.shape
+        assert (nh, hd) == (H, D) and k_cache8.dtype == np.uint8 and v_cache8.shape == k_cache8.shape
+        kc = np.ascontiguousarray(k_cache8)
+        vc = np.ascontiguousarray(v_cache8)
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        qs = np.ascontiguousarray(query_start, dtype=np.int32)
+        S = cl.shape[0]
+        out = np.zeros((T, H, D), dtype=np.float64)
+        used = np.zeros(1, dtype=np.int32)
+        rc = self.lib.oracle_prefill_fp8(_ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt),
+                                         _ptr(cl), _ptr(qs), S, T, H, D, nb, bs, bt.shape[1],
+                                         float(scale), float(k_scale), float(v_scale), _ptr(used))
+        if rc:
+            raise ValueError(f"oracle_prefill_fp8 failed ({rc})")
         self.threads_used = int(used[0])
         return out
 

@@ -539,12 +539,16 @@ int oracle_decode_fp8_pairs(double *out, const int32_t *pairs, int32_t num_pairs
  * q and out are [num_tokens, num_heads, head_dim] with the rows of sequence s
  * at query_start[s] .. query_start[s+1]-1.
  * ------------------------------------------------------------------------- */
-int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
-                   const uint16_t *v_cache, const int32_t *block_tables,
-                   const int32_t *context_lens, const int32_t *query_start, int32_t num_seqs,
-                   int32_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
-                   int32_t block_size, int32_t max_blocks_per_seq, double scale,
-                   int32_t *threads_used)
+/* One body for both cache formats: fp16 caches (k_cache, v_cache), or FP8
+ * codes (k8, v8, non-NULL) dequantised with k_scale, v_scale as in the FP8
+ * decode. */
+static int prefill_any(double *out, const uint16_t *q, const uint16_t *k_cache,
+                       const uint16_t *v_cache, const uint8_t *k8, const uint8_t *v8,
+                       float k_scale, float v_scale, const int32_t *block_tables,
+                       const int32_t *context_lens, const int32_t *query_start,
+                       int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                       int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                       int32_t max_blocks_per_seq, double scale, int32_t *threads_used)
 {
     int rc = check_shapes(num_seqs, num_heads, head_dim, num_blocks, block_size,
                           max_blocks_per_seq);
@@ -577,9 +581,12 @@ int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
             if (local)
                 continue;
             int32_t s = (int32_t)(u / num_heads), h = (int32_t)(u % num_heads);
-            int L = oracle_gather(Kbuf, Vbuf, k_cache, v_cache, block_tables, context_lens, s, h,
-                                  num_heads, head_dim, num_blocks, block_size,
-                                  max_blocks_per_seq);
+            int L = k8 ? gather_fp8(Kbuf, Vbuf, k8, v8, block_tables, context_lens, s, h,
+                                    num_heads, head_dim, num_blocks, block_size,
+                                    max_blocks_per_seq, k_scale, v_scale)
+                       : oracle_gather(Kbuf, Vbuf, k_cache, v_cache, block_tables, context_lens,
+                                       s, h, num_heads, head_dim, num_blocks, block_size,
+                                       max_blocks_per_seq);
             if (L < 0) {
                 local = L;
                 continue;
@@ -605,6 +612,34 @@ int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
     if (threads_used)
         *threads_used = nthreads;
     return status;
+}
+
+int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
+                   const uint16_t *v_cache, const int32_t *block_tables,
+                   const int32_t *context_lens, const int32_t *query_start, int32_t num_seqs,
+                   int32_t num_tokens, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                   int32_t block_size, int32_t max_blocks_per_seq, double scale,
+                   int32_t *threads_used)
+{
+    return prefill_any(out, q, k_cache, v_cache, NULL, NULL, 1.0f, 1.0f, block_tables,
+                       context_lens, query_start, num_seqs, num_tokens, num_heads, head_dim,
+                       num_blocks, block_size, max_blocks_per_seq, scale, threads_used);
+}
+
+/* Multi-query paged attention over FP8 caches: oracle_prefill with each K
+ * (V) value read as value(code) * k_scale (v_scale), q still fp16. */
+int oracle_prefill_fp8(double *out, const uint16_t *q, const uint8_t *k_cache,
+                       const uint8_t *v_cache, const int32_t *block_tables,
+                       const int32_t *context_lens, const int32_t *query_start,
+                       int32_t num_seqs, int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                       int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                       double scale, float k_scale, float v_scale, int32_t *threads_used)
+{
+    if (!k_cache || !v_cache)
+        return OR_ERR_ARG;
+    return prefill_any(out, q, NULL, NULL, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, query_start, num_seqs, num_tokens, num_heads, head_dim,
+                       num_blocks, block_size, max_blocks_per_seq, scale, threads_used);
 }
 
 /* Timing plumbing, no arithmetic: the number of host threads later calls use

@@ -558,12 +558,58 @@ def pin_prefill_brute_force(orc):
                 assert np.allclose(got[qs[s] + i, 0], ref, rtol=1e-11, atol=1e-13), (B, s, i)
 
 
+def _fp8_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape, dtype=np.uint32).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x3C   # no NaN codes in live data
+    return c
+
+
+def pin_prefill_fp8_sdpa_causal(orc):
+    """FP8 prefill against torch's own E4M3 decoding and causal SDPA in fp64,
+    through a scattered table."""
+    import torch
+    rng = np.random.default_rng(17)
+    lens, nq = [40, 17, 64], [40, 5, 1]
+    H, D, B = 2, 64, 16
+    q, _, _, bt, cl, qs, MB = _prefill_case(rng, lens, nq, H, D, B)
+    NB = int(bt.max()) + 1
+    kc, vc = _fp8_codes(rng, (NB, B, H, D)), _fp8_codes(rng, (NB, B, H, D))
+    ks, vs = 0.02, 0.125
+    got = orc.prefill_fp8(q, kc, vc, bt, cl, qs, 0.125, ks, vs)
+    Kd = torch.from_numpy(kc).view(torch.float8_e4m3fn).double() * float(np.float32(ks))
+    Vd = torch.from_numpy(vc).view(torch.float8_e4m3fn).double() * float(np.float32(vs))
+    for s in range(len(lens)):
+        L, n = lens[s], nq[s]
+        idx = [int(bt[s][t // B]) * B + t % B for t in range(L)]
+        Kc = Kd.reshape(NB * B, H, D)[idx]
+        Vc = Vd.reshape(NB * B, H, D)[idx]
+        Q = torch.from_numpy(q[qs[s]:qs[s + 1]].astype(np.float64))
+        allowed = torch.arange(L)[None, :] <= (L - n + torch.arange(n))[:, None]
+        for h in range(H):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                Q[:, h].reshape(1, n, D).contiguous(), Kc[:, h].reshape(1, L, D).contiguous(),
+                Vc[:, h].reshape(1, L, D).contiguous(), attn_mask=allowed.reshape(1, n, L),
+                scale=0.125).reshape(n, D).numpy()
+            assert np.allclose(got[qs[s]:qs[s + 1], h], ref, rtol=1e-11, atol=1e-13), (s, h)
+
+
+def pin_prefill_fp8_single_query_is_decode(orc):
+    rng = np.random.default_rng(18)
+    q, _, _, bt, cl, qs, _ = _prefill_case(rng, [1, 30, 77, 16], [1, 1, 1, 1], 2, 64, 16)
+    NB = int(bt.max()) + 1
+    kc, vc = _fp8_codes(rng, (NB, 16, 2, 64)), _fp8_codes(rng, (NB, 16, 2, 64))
+    a = orc.prefill_fp8(q, kc, vc, bt, cl, qs, 0.125, 0.5, 0.03)
+    b = orc.decode_fp8(q, kc, vc, bt, cl, 0.125, 0.5, 0.03)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
 PINS = [pin_half_decode_exhaustive, pin_gather_worked_example, pin_contiguous_sdpa,
         pin_block_permutation_invariance, pin_brute_force_tiny, pin_closed_forms, pin_needles,
         pin_reshape_scatter, pin_reshape_worked_example, pin_copy_blocks, pin_copy_on_write,
         pin_swap_blocks, pin_e4m3_decode_exhaustive, pin_e4m3_encode, pin_quantize_scale,
         pin_fp8_decode_sdpa, pin_fp8_reshape, pin_prefill_single_query_is_decode,
-        pin_prefill_sdpa_causal, pin_prefill_brute_force]
+        pin_prefill_sdpa_causal, pin_prefill_brute_force, pin_prefill_fp8_sdpa_causal,
+        pin_prefill_fp8_single_query_is_decode]
 
 
 def main(argv):

@@ -75,6 +75,10 @@ MUTANTS = {
     "prefill_sees_everything": ("int32_t visible = L - n + i + 1;", "int32_t visible = L;"),
     "prefill_rows_reversed": ("int32_t row = query_start[s] + i;",
                               "int32_t row = query_start[s + 1] - 1 - i;"),
+    "prefill_fp8_scales_swapped": ("max_blocks_per_seq, k_scale, v_scale)",
+                                   "max_blocks_per_seq, v_scale, k_scale)"),
+    "prefill_fp8_v_scale_as_k": ("k_cache, v_cache, k_scale, v_scale, block_tables,",
+                                 "k_cache, v_cache, k_scale, k_scale, block_tables,"),
 }
 
 
