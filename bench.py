@@ -237,21 +237,25 @@ def bench_blocks(op, pairs, iters, cpu=None):
 MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 
 
-def bench_cascade(iters, warmup, cpu=None):
+def bench_cascade(iters, warmup, cpu=None, fp8=False):
     """Shared-prefix step (config 3) with the prefix read once per 64
     sequences: pa_decode_cascade_append (the new tokens are written by the
     prefix pass's launch); the same step as two calls (reshape_and_cache +
-    pa_decode_cascade) is reported beside it."""
+    pa_decode_cascade) is reported beside it.  FP8 caches: the two calls
+    reshape_and_cache_fp8 + pa_decode_cascade_fp8 are the step."""
     import numpy as np
     import torch
     import paged_kv_cache_155_amd as pa
-    from paged_kv_cache_155_amd.workloads import DESCRIPTIONS, make_workload, split_shared_prefix
+    from paged_kv_cache_155_amd.workloads import (DESCRIPTIONS, fp8_pools, make_workload,
+                                                  split_shared_prefix)
     w = make_workload(3, poison=False)
     prefix, plen, st, sl = split_shared_prefix(w, 32)
 
     def up(x):
         return torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    kc, vc, q = up(w.k_cache), up(w.v_cache), up(w.q)
+    f8 = fp8_pools(w) if fp8 else None
+    kc, vc = (up(f8.k_cache), up(f8.v_cache)) if fp8 else (up(w.k_cache), up(w.v_cache))
+    q = up(w.q)
     key, val, slots = up(w.key), up(w.value), up(w.slot_mapping)
     pt, stt, slt = up(prefix), up(st), up(sl)
     out = torch.empty_like(q)
@@ -261,21 +265,39 @@ def bench_cascade(iters, warmup, cpu=None):
                      dtype=torch.uint8, device="cuda")
     scale = float(w.scale)
     stream = torch.cuda.current_stream()
+
+    def reshape():
+        if fp8:
+            pa.reshape_and_cache_fp8(key, val, kc, vc, slots, f8.k_scale, f8.v_scale)
+        else:
+            pa.reshape_and_cache(key, val, kc, vc, slots)
+
+    def decode():
+        if fp8:
+            pa.decode_cascade_fp8(out, q, kc, vc, pt, plen, stt, slt, scale, f8.k_scale,
+                                  f8.v_scale, P, ws)
+        else:
+            pa.decode_cascade(out, q, kc, vc, pt, plen, stt, slt, scale, P, ws)
+
     def step():
-        pa.decode_cascade_append(out, q, key, val, kc, vc, slots, pt, plen, stt, slt, scale, P,
-                                 ws)
+        if fp8:  # no one-call form over FP8 caches
+            reshape()
+            decode()
+        else:
+            pa.decode_cascade_append(out, q, key, val, kc, vc, slots, pt, plen, stt, slt, scale,
+                                     P, ws)
     for _ in range(warmup):
-        pa.reshape_and_cache(key, val, kc, vc, slots)
-        pa.decode_cascade(out, q, kc, vc, pt, plen, stt, slt, scale, P, ws)
+        reshape()
+        decode()
         step()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
     t0 = time.perf_counter()
     for e in ev:
         e[0].record(stream)
-        pa.reshape_and_cache(key, val, kc, vc, slots)
+        reshape()
         e[1].record(stream)
-        pa.decode_cascade(out, q, kc, vc, pt, plen, stt, slt, scale, P, ws)
+        decode()
         e[2].record(stream)
     torch.cuda.synchronize()
     step_ms = (time.perf_counter() - t0) * 1e3 / iters
@@ -286,15 +308,15 @@ def bench_cascade(iters, warmup, cpu=None):
     d1 = torch.cuda.Event(enable_timing=True)
     d0.record(stream)
     for _ in range(iters):
-        pa.decode_cascade(out, q, kc, vc, pt, plen, stt, slt, scale, P, ws)
+        decode()
     d1.record(stream)
     torch.cuda.synchronize()
     dec = d0.elapsed_time(d1) / iters
     # the step as two calls (reshape_and_cache + decode) back to back
     d0.record(stream)
     for _ in range(iters):
-        pa.reshape_and_cache(key, val, kc, vc, slots)
-        pa.decode_cascade(out, q, kc, vc, pt, plen, stt, slt, scale, P, ws)
+        reshape()
+        decode()
     d1.record(stream)
     torch.cuda.synchronize()
     step_two = d0.elapsed_time(d1) / iters
@@ -305,15 +327,27 @@ def bench_cascade(iters, warmup, cpu=None):
     d1.record(stream)
     torch.cuda.synchronize()
     step_gpu = d0.elapsed_time(d1) / iters
-    uniq, logical = w.unique_kv_bytes(), w.kv_bytes()
+    eb = 1 if fp8 else 2  # bytes per cache element
+    uniq, logical = w.unique_kv_bytes() * eb // 2, w.kv_bytes() * eb // 2
     line_cpu = None
     if cpu is not None:  # the oracle's decode over the full tables, whole workload
         import oracle
         orc = oracle.get()
-        okc, ovc = w.k_cache.copy(), w.v_cache.copy()
-        orc.reshape_and_cache(w.key, w.value, okc, ovc, w.slot_mapping)
-        dt, runs = _time_oracle(lambda: orc.decode(w.q, okc, ovc, w.block_tables, w.context_lens,
-                                                   scale), cpu.cpu_repeats, cpu.cpu_seconds)
+        if fp8:
+            okc, ovc = f8.k_cache.copy(), f8.v_cache.copy()
+            orc.reshape_and_cache_fp8(w.key, w.value, okc, ovc, w.slot_mapping, f8.k_scale,
+                                      f8.v_scale)
+
+            def run():
+                return orc.decode_fp8(w.q, okc, ovc, w.block_tables, w.context_lens, scale,
+                                      f8.k_scale, f8.v_scale)
+        else:
+            okc, ovc = w.k_cache.copy(), w.v_cache.copy()
+            orc.reshape_and_cache(w.key, w.value, okc, ovc, w.slot_mapping)
+
+            def run():
+                return orc.decode(w.q, okc, ovc, w.block_tables, w.context_lens, scale)
+        dt, runs = _time_oracle(run, cpu.cpu_repeats, cpu.cpu_seconds)
         line_cpu = {"value": round(uniq / dt / 1e9, 4), "unit": "GB/s (unique K/V bytes)",
                     "cores": orc.threads_used, "kind": "oracle",
                     "sample": f"the whole workload ({w.num_seqs} seqs x {w.num_heads} heads over "
@@ -322,11 +356,13 @@ def bench_cascade(iters, warmup, cpu=None):
                               f"{w.num_seqs / dt:.1f} tokens/s/layer"}
     print(json.dumps({
         "op": "cascade", "workload": f"config3: {DESCRIPTIONS[3]}", "partition_size": P,
+        "kv_dtype": "fp8-e4m3" if fp8 else "fp16",
         "t_decode_us_mean": round(dec * 1e3, 2),
         "t_decode_us_events_mean": round(dec_events * 1e3, 2),
         "t_reshape_us_mean": round(rc * 1e3, 2),
         "wall_ms_per_step": round(step_ms, 4), "ms_per_step": round(step_gpu, 6),
-        "step": "pa_decode_cascade_append",
+        "step": ("reshape_and_cache_fp8 + pa_decode_cascade_fp8" if fp8
+                 else "pa_decode_cascade_append"),
         "ms_per_step_two_calls": round(step_two, 6),
         "decode_tokens_per_s_per_layer": round(w.num_seqs / (step_gpu * 1e-3), 1),
         "kv_bytes_logical": logical, "kv_bytes_unique": uniq,
@@ -334,60 +370,79 @@ def bench_cascade(iters, warmup, cpu=None):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(uniq / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "bytes": "unique K/V bytes",
-                     "kernel": "pa_decode_cascade (prefix pass + partition kernel): HIP events "
-                               "around calls back to back",
-                     "traffic": _traffic("cascade_config3_B16_P0", "cascade")},
+                     "kernel": ("pa_decode_cascade_fp8" if fp8 else "pa_decode_cascade")
+                               + " (prefix pass + partition kernel): HIP events around calls "
+                               "back to back",
+                     "traffic": None if fp8 else _traffic("cascade_config3_B16_P0", "cascade")},
         "logical_kv_gbs": round(logical / (dec * 1e-3) / 1e9, 1),
         "cpu_baseline": line_cpu}), flush=True)
 
 
-def bench_multi_query(iters, warmup, cpu=None):
+def bench_multi_query(iters, warmup, cpu=None, fp8=False):
     """A chunked-prefill batch: 16 sequences of 2048 positions whose last 512
-    are this step's new tokens (32 heads x 128, B = 16)."""
+    are this step's new tokens (32 heads x 128, B = 16); fp16 or FP8 caches
+    (the matrix-core products are fp16 either way)."""
     import numpy as np
     import torch
     import paged_kv_cache_155_amd as pa
-    from paged_kv_cache_155_amd.workloads import make_multi_query
+    from paged_kv_cache_155_amd.workloads import fp8_pools, make_multi_query
     S, ctx, n = 16, 2048, 512
     w, qh, qs = make_multi_query([ctx] * S, [n] * S, 32, 128, 16, seed=155, poison=False)
 
     def up(x):
         return torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    kc, vc, q = up(w.k_cache), up(w.v_cache), up(qh)
+    f8 = fp8_pools(w) if fp8 else None
+    kc, vc = (up(f8.k_cache), up(f8.v_cache)) if fp8 else (up(w.k_cache), up(w.v_cache))
+    q = up(qh)
     bt, cl, qst = up(w.block_tables), up(w.context_lens), up(qs)
     out = torch.empty_like(q)
     scale = float(w.scale)
+
+    def call():
+        if fp8:
+            pa.multi_query_fp8(out, q, kc, vc, bt, cl, qst, n, scale, f8.k_scale, f8.v_scale)
+        else:
+            pa.multi_query(out, q, kc, vc, bt, cl, qst, n, scale)
     # at least 100 untimed calls (~35 ms): the matrix-core clock settles over the first ~20 ms
-    ms = _time_events(lambda: pa.multi_query(out, q, kc, vc, bt, cl, qst, n, scale), iters,
-                      max(warmup, 100))
+    ms = _time_events(call, iters, max(warmup, 100))
     t = float(np.median(ms)) * 1e-3
     H, D = w.num_heads, w.head_dim
     visible = sum(ctx - n + i + 1 for i in range(n)) * S          # (row, key) pairs per head
     flops = 4.0 * D * visible * H                                   # q.k and p.v
-    kv_unique = S * ctx * H * D * 2 * 2
+    kv_unique = S * ctx * H * D * 2 * (1 if fp8 else 2)
     line_cpu = None
     if cpu is not None:  # the oracle's prefill on the first 2 of the 16 sequences
         import oracle
         orc = oracle.get()
         ns = 2
         sq = qh[qs[0]:qs[ns]]
-        dt, runs = _time_oracle(lambda: orc.prefill(sq, w.k_cache, w.v_cache, w.block_tables[:ns],
-                                                    w.context_lens[:ns], qs[:ns + 1], scale),
-                                cpu.cpu_repeats, cpu.cpu_seconds)
+        if fp8:
+            def run():
+                return orc.prefill_fp8(sq, f8.k_cache, f8.v_cache, w.block_tables[:ns],
+                                       w.context_lens[:ns], qs[:ns + 1], scale, f8.k_scale,
+                                       f8.v_scale)
+        else:
+            def run():
+                return orc.prefill(sq, w.k_cache, w.v_cache, w.block_tables[:ns],
+                                   w.context_lens[:ns], qs[:ns + 1], scale)
+        dt, runs = _time_oracle(run, cpu.cpu_repeats, cpu.cpu_seconds)
         sflops = flops * ns / S
         line_cpu = {"value": round(sflops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": orc.threads_used,
                     "kind": "oracle",
                     "sample": f"{ns} of {S} sequences ({ns * n} query rows x {H} heads); fp64 "
-                              f"oracle prefill, median of {runs} runs = {dt:.3f} s wall on "
+                              f"oracle {'FP8 ' if fp8 else ''}prefill, median of {runs} runs = "
+                              f"{dt:.3f} s wall on "
                               f"{orc.threads_used} threads; {ns * n / dt:.1f} query rows/s"}
     print(json.dumps({
         "op": "multi_query", "workload": f"{S} seqs x {ctx} positions, last {n} new, 32 heads x 128",
+        "kv_dtype": "fp8-e4m3" if fp8 else "fp16",
         "rows": S * n, "us_median": round(t * 1e6, 2),
         "query_tokens_per_s": round(S * n / t, 1),
         "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 2),
                      "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / t / 1e12 / MFMA_F16_TFLOPS, 4),
-                     "traffic": _traffic("multi_query_16x2048_last512", "multi_query")},
+                     "traffic": None if fp8 else _traffic("multi_query_16x2048_last512",
+                                                          "multi_query")},
         "kv_unique_gbs": round(kv_unique / t / 1e9, 1), "cpu_baseline": line_cpu}), flush=True)
 
 
@@ -523,10 +578,12 @@ def main():
         probe_copy(a.probe_mib)
         return
     if a.op == "cascade":
-        bench_cascade(a.steps, a.warmup, None if a.no_cpu_baseline else a)
+        bench_cascade(a.steps, a.warmup, None if a.no_cpu_baseline else a,
+                      fp8=a.kv_dtype == "fp8")
         return
     if a.op == "multi_query":
-        bench_multi_query(a.steps, a.warmup, None if a.no_cpu_baseline else a)
+        bench_multi_query(a.steps, a.warmup, None if a.no_cpu_baseline else a,
+                          fp8=a.kv_dtype == "fp8")
         return
     if a.op != "step":
         bench_blocks(a.op, a.pairs, a.steps, None if a.no_cpu_baseline else a)

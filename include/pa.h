@@ -268,6 +268,37 @@ int pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_cascade over FP8 caches: the same arguments, semantics,
+ * workspace (pa_decode_cascade_workspace_size) and errors as
+ * pa_decode_cascade, with k_cache / v_cache holding E4M3 codes dequantised
+ * as in pa_decode_fp8 (k_scale, v_scale finite and > 0, else
+ * PA_ERR_INVALID_DIM).  The prefix pass widens each staged code exactly to
+ * fp16 for the matrix-core products; the K scale is folded into the logit
+ * scale and the V scale into the rows.  prefix_len = 0 is pa_decode_fp8.
+ */
+int pa_decode_cascade_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* prefix_block_table, int32_t prefix_len,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                          int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                          float scale, float k_scale, float v_scale, int32_t partition_size,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_multi_query over FP8 caches: the same arguments, semantics and errors as
+ * pa_multi_query, with k_cache / v_cache holding E4M3 codes dequantised as in
+ * pa_decode_fp8 (k_scale, v_scale finite and > 0, else PA_ERR_INVALID_DIM).
+ * Staging widens each code exactly to fp16 for the matrix-core products;
+ * the K scale is folded into the logit scale and the V scale into the rows.
+ */
+int pa_multi_query_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                       int32_t max_query_len, int32_t num_heads, int32_t head_dim,
+                       int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                       float scale, float k_scale, float v_scale, void* stream);
+
+/*
  * Copy whole physical blocks inside one cache pair: the copy-on-write step
  * of [arch] §2.3 (a sequence about to write into a block it shares gets a
  * private copy, and its table is then pointed at the copy by the caller).

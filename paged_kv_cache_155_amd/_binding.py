@@ -58,8 +58,14 @@ def load(path=None):
     lib.pa_decode_cascade_append.argtypes = ([_P] * 8 + [_I32] + [_P] * 2 + [_I32] * 6
                                              + [ctypes.c_float, _I32, _P, ctypes.c_size_t, _P])
     lib.pa_decode_cascade_append.restype = ctypes.c_int
+    lib.pa_decode_cascade_fp8.argtypes = ([_P] * 5 + [_I32] + [_P] * 2 + [_I32] * 6
+                                          + [ctypes.c_float] * 3
+                                          + [_I32, _P, ctypes.c_size_t, _P])
+    lib.pa_decode_cascade_fp8.restype = ctypes.c_int
     lib.pa_multi_query.argtypes = [_P] * 7 + [_I32] * 8 + [ctypes.c_float, _P]
     lib.pa_multi_query.restype = ctypes.c_int
+    lib.pa_multi_query_fp8.argtypes = [_P] * 7 + [_I32] * 8 + [ctypes.c_float] * 3 + [_P]
+    lib.pa_multi_query_fp8.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_swap_blocks.argtypes = [_P, _P, _P, _I32, _I32, _I32, ctypes.c_int64, _P]
@@ -311,6 +317,40 @@ def decode_cascade(out, q, k_cache, v_cache, prefix_table, prefix_len, block_tab
     return out
 
 
+def decode_cascade_fp8(out, q, k_cache, v_cache, prefix_table, prefix_len, block_tables,
+                       context_lens, scale, k_scale, v_scale, partition_size=512, workspace=None,
+                       stream=None):
+    """decode_cascade() over FP8 caches (values = code * scale, as decode_fp8)."""
+    import torch
+    _check_fp8_cache(k_cache, "k_cache")
+    NB, B, H, D = k_cache.shape
+    _check_fp8_cache(v_cache, "v_cache", shape=k_cache.shape)
+    _check(q, "q", torch.float16, ndim=3)
+    S = q.shape[0]
+    _check(q, "q", torch.float16, shape=(S, H, D))
+    _check(out, "out", torch.float16, shape=(S, H, D))
+    _check(prefix_table, "prefix_table", torch.int32, ndim=1)
+    if prefix_len % B or prefix_table.numel() * B < prefix_len:
+        raise ValueError("prefix_len must be a multiple of the block size covered by prefix_table")
+    _check(block_tables, "block_tables", torch.int32, ndim=2)
+    MB = block_tables.shape[1]
+    _check(block_tables, "block_tables", torch.int32, shape=(S, MB))
+    _check(context_lens, "context_lens", torch.int32, shape=(S,))
+    need = decode_cascade_workspace_size(S, H, D, B, int(prefix_len), MB, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check(workspace, "workspace", torch.uint8, ndim=1)
+    rc = load().pa_decode_cascade_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(prefix_table), int(prefix_len), _ptr(block_tables),
+                                      _ptr(context_lens), S, H, D, NB, B, MB, float(scale),
+                                      float(k_scale), float(v_scale), int(partition_size),
+                                      _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_decode_cascade_fp8")
+    return out
+
+
 def decode_cascade_append(out, q, key, value, k_cache, v_cache, slot_mapping, prefix_table,
                           prefix_len, block_tables, context_lens, scale, partition_size=512,
                           workspace=None, stream=None):
@@ -373,4 +413,28 @@ def multi_query(out, q, k_cache, v_cache, block_tables, context_lens, query_star
                                _stream_ptr(stream))
     if rc != PA_OK:
         raise PAError(rc, "pa_multi_query")
+    return out
+
+
+def multi_query_fp8(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                    max_query_len, scale, k_scale, v_scale, stream=None):
+    """multi_query() over FP8 caches (values = code * scale, as decode_fp8)."""
+    import torch
+    _check_fp8_cache(k_cache, "k_cache")
+    NB, B, H, D = k_cache.shape
+    _check_fp8_cache(v_cache, "v_cache", shape=k_cache.shape)
+    _check(q, "q", torch.float16, ndim=3)
+    T = q.shape[0]
+    _check(q, "q", torch.float16, shape=(T, H, D))
+    _check(out, "out", torch.float16, shape=(T, H, D))
+    _check(block_tables, "block_tables", torch.int32, ndim=2)
+    S, MB = block_tables.shape
+    _check(context_lens, "context_lens", torch.int32, shape=(S,))
+    _check(query_start, "query_start", torch.int32, shape=(S + 1,))
+    rc = load().pa_multi_query_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_tables), _ptr(context_lens), _ptr(query_start), S,
+                                   T, int(max_query_len), H, D, NB, B, MB, float(scale),
+                                   float(k_scale), float(v_scale), _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_multi_query_fp8")
     return out

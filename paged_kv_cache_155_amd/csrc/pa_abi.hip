@@ -209,23 +209,37 @@ size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads, int
 
 namespace {
 
-// pa_decode_cascade, and pa_decode_cascade_append when key != nullptr
+// FP8 caches: the dequantisation scales of K and V
+struct Fp8Scales {
+    float k, v;
+};
+
+// pa_decode_cascade; pa_decode_cascade_append when append (fp16 only);
+// pa_decode_cascade_fp8 when fp8 != nullptr
 int cascade(void* out, const void* q, const void* key, const void* value, void* k_cache,
             void* v_cache, const int64_t* slot_mapping, const int32_t* prefix_block_table,
             int32_t prefix_len, const int32_t* block_tables, const int32_t* context_lens,
             int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
             int32_t block_size, int32_t max_blocks_per_seq, float scale, int32_t partition_size,
-            void* workspace, size_t workspace_bytes, void* stream, bool append)
+            void* workspace, size_t workspace_bytes, void* stream, bool append,
+            const Fp8Scales* fp8 = nullptr)
 {
     if (prefix_len < 0 || (block_size > 0 && prefix_len % block_size != 0))
         return PA_ERR_INVALID_DIM;
     if (!(std::isfinite(scale) && scale > 0.0f))
+        return PA_ERR_INVALID_DIM;
+    if (fp8 && (!valid_scale(fp8->k) || !valid_scale(fp8->v)))
         return PA_ERR_INVALID_DIM;
     if (append && (!key || !value || !slot_mapping) && num_seqs > 0)
         return PA_ERR_NULL;
     if (append && num_seqs > 0 &&
         (!aligned16(key) || !aligned16(value) || (reinterpret_cast<uintptr_t>(slot_mapping) & 7u)))
         return PA_ERR_ALIGN;
+    if (prefix_len == 0 && fp8)  // nothing shared: the plain decode
+        return pa_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                             num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
+                             scale, fp8->k, fp8->v, partition_size, workspace, workspace_bytes,
+                             stream);
     if (prefix_len == 0) {  // nothing shared: the plain step (its own write, then pa_decode)
         if (!append)
             return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
@@ -257,6 +271,10 @@ int cascade(void* out, const void* q, const void* key, const void* value, void* 
         return rc == 1 ? PA_OK : rc;
     if (!prefix_block_table)
         return PA_ERR_NULL;
+    if (fp8) {  // the K scale folds into the logit scale, the V scale into the rows
+        p.scale_log2 = (float)((double)scale * (double)fp8->k * 1.4426950408889634074);
+        p.v_scale = fp8->v;
+    }
     const int64_t row_tiles = ((int64_t)num_seqs + pa::kCascadeTileRows - 1) / pa::kCascadeTileRows;
     if (row_tiles * num_heads * parts > INT32_MAX || !grid_fits(row_tiles * num_heads * parts))
         return PA_ERR_INVALID_DIM;
@@ -277,6 +295,7 @@ int cascade(void* out, const void* q, const void* key, const void* value, void* 
     m.row_tiles = (int32_t)row_tiles;
     m.total_units = (uint32_t)(row_tiles * parts * num_heads);
     m.scale_log2 = p.scale_log2;
+    m.v_scale = p.v_scale;
     if (append) {  // the prefix pass also writes the new tokens (into private suffix slots)
         m.new_k = static_cast<const _Float16*>(key);
         m.new_v = static_cast<const _Float16*>(value);
@@ -293,9 +312,11 @@ int cascade(void* out, const void* q, const void* key, const void* value, void* 
     // every suffix fits one partition the partition kernel merges the prefix
     // slots itself and writes the rows, else the reduce merges all slots.
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = pa::launch_cascade_prefix(m, head_dim, block_size, st);
+    hipError_t e = fp8 ? pa::launch_cascade_prefix_fp8(m, head_dim, block_size, st)
+                       : pa::launch_cascade_prefix(m, head_dim, block_size, st);
     if (e == hipSuccess)
-        e = pa::launch_decode_dispatch(p, head_dim, block_size, st);
+        e = fp8 ? pa::launch_decode_fp8_dispatch(p, head_dim, block_size, st)
+                : pa::launch_decode_dispatch(p, head_dim, block_size, st);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -315,6 +336,22 @@ int pa_decode_cascade(void* out, const void* q, const void* k_cache, const void*
                    workspace_bytes, stream, /*append=*/false);
 }
 
+int pa_decode_cascade_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* prefix_block_table, int32_t prefix_len,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                          int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                          float scale, float k_scale, float v_scale, int32_t partition_size,
+                          void* workspace, size_t workspace_bytes, void* stream)
+{
+    const Fp8Scales sc{k_scale, v_scale};
+    return cascade(out, q, nullptr, nullptr, const_cast<void*>(k_cache),
+                   const_cast<void*>(v_cache), nullptr, prefix_block_table, prefix_len,
+                   block_tables, context_lens, num_seqs, num_heads, head_dim, num_blocks,
+                   block_size, max_blocks_per_seq, scale, partition_size, workspace,
+                   workspace_bytes, stream, /*append=*/false, &sc);
+}
+
 int pa_decode_cascade_append(void* out, const void* q, const void* key, const void* value,
                              void* k_cache, void* v_cache, const int64_t* slot_mapping,
                              const int32_t* prefix_block_table, int32_t prefix_len,
@@ -330,12 +367,18 @@ int pa_decode_cascade_append(void* out, const void* q, const void* key, const vo
                    workspace_bytes, stream, /*append=*/true);
 }
 
-int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,
-                   const int32_t* block_tables, const int32_t* context_lens,
-                   const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
-                   int32_t max_query_len, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
-                   int32_t block_size, int32_t max_blocks_per_seq, float scale, void* stream)
+namespace {
+
+// pa_multi_query; pa_multi_query_fp8 when fp8 != nullptr
+int multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens,
+                const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                int32_t max_query_len, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                int32_t block_size, int32_t max_blocks_per_seq, float scale, void* stream,
+                const Fp8Scales* fp8)
 {
+    if (fp8 && (!valid_scale(fp8->k) || !valid_scale(fp8->v)))
+        return PA_ERR_INVALID_DIM;
     if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_heads <= 0 || head_dim <= 0 ||
         num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0)
         return PA_ERR_INVALID_DIM;
@@ -370,10 +413,39 @@ int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_
     m.max_blocks_per_seq = max_blocks_per_seq;
     m.row_tiles = (int32_t)tiles;
     m.total_units = (uint32_t)units;
-    m.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    hipError_t e = pa::launch_multiquery(m, head_dim, block_size,
-                                         static_cast<hipStream_t>(stream));
+    m.scale_log2 = (float)((double)scale * (fp8 ? (double)fp8->k : 1.0) * 1.4426950408889634074);
+    m.v_scale = fp8 ? fp8->v : 1.0f;
+    hipError_t e = fp8 ? pa::launch_multiquery_fp8(m, head_dim, block_size,
+                                                   static_cast<hipStream_t>(stream))
+                       : pa::launch_multiquery(m, head_dim, block_size,
+                                               static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+int pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                   int32_t max_query_len, int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                   int32_t block_size, int32_t max_blocks_per_seq, float scale, void* stream)
+{
+    return multi_query(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                       num_seqs, num_tokens, max_query_len, num_heads, head_dim, num_blocks,
+                       block_size, max_blocks_per_seq, scale, stream, nullptr);
+}
+
+int pa_multi_query_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start, int32_t num_seqs, int32_t num_tokens,
+                       int32_t max_query_len, int32_t num_heads, int32_t head_dim,
+                       int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                       float scale, float k_scale, float v_scale, void* stream)
+{
+    const Fp8Scales sc{k_scale, v_scale};
+    return multi_query(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                       num_seqs, num_tokens, max_query_len, num_heads, head_dim, num_blocks,
+                       block_size, max_blocks_per_seq, scale, stream, &sc);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -42,8 +42,8 @@ struct MqParams {
     float* ws_m;
     float* ws_l;
     const _Float16* q;             // multi-query: [T, H, D]; shared prefix: [S, H, D]
-    const _Float16* k_cache;
-    const _Float16* v_cache;
+    const void* k_cache;           // fp16, or FP8 codes (the _fp8 launches)
+    const void* v_cache;
     const int32_t* block_tables;   // multi-query: [S, MB]
     const int32_t* context_lens;   // multi-query: [S] (including the new tokens)
     const int32_t* query_start;    // multi-query: [S + 1]
@@ -59,7 +59,8 @@ struct MqParams {
     int32_t prefix_parts;          // shared prefix: partitions = workspace slots 0..parts-1
     int32_t num_slots;             // shared prefix: workspace slots per (s, h)
     uint32_t total_units;          // workgroups of query-row tiles
-    float scale_log2;
+    float scale_log2;              // scale * log2(e) (times the K scale for FP8)
+    float v_scale;                 // FP8: dequantisation scale of V
     uint32_t copy_units;           // shared prefix, appending form: copy workgroups first
     // shared prefix, appending form (new_k == nullptr otherwise): row s of
     // new_k / new_v [S, H, D] goes to cache slot slot_mapping[s] when
@@ -73,10 +74,14 @@ struct MqParams {
 };
 
 hipError_t launch_multiquery(const MqParams& p, int head_dim, int block_size, hipStream_t stream);
+hipError_t launch_multiquery_fp8(const MqParams& p, int head_dim, int block_size,
+                                 hipStream_t stream);
 // extra workgroups of the appending shared-prefix pass (0 unless p.new_k)
 int64_t copy_workgroups(const MqParams& p, int head_dim);
 hipError_t launch_cascade_prefix(const MqParams& p, int head_dim, int block_size,
                                  hipStream_t stream);
+hipError_t launch_cascade_prefix_fp8(const MqParams& p, int head_dim, int block_size,
+                                     hipStream_t stream);
 
 // partition kernel + (if num_slots > 1) the log-sum-exp reduce
 hipError_t launch_decode_dispatch(const DecodeParams& p, int head_dim, int block_size,

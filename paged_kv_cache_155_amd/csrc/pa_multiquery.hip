@@ -67,6 +67,25 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ h8 as_h8(const u32x4& v) { return __builtin_bit_cast(h8, v); }
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// K/V elements as they lie in the cache: 8 fp16 values (16 bytes), or 8 FP8
+// (OCP E4M3) codes (8 bytes) that staging widens exactly to fp16 (every E4M3
+// value is an fp16 value; the cache scales are applied outside the tile).
+template <bool kFp8> struct Raw8 { typedef u32x4 type; };
+template <> struct Raw8<true> { typedef u32x2 type; };
+
+__device__ __forceinline__ u32x4 widen8(const u32x4& v) { return v; }
+__device__ __forceinline__ u32x4 widen8(const u32x2& v)
+{
+    const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.0f, false);  // bytes 0, 1
+    const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, 1.0f, true);   // bytes 2, 3
+    const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.0f, false);
+    const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, 1.0f, true);
+    return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                 __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+}
+
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s4 lds_s4;
 // ds_read_b64_tr_b16 (transposing LDS read; 8-byte aligned LDS address)
@@ -154,7 +173,7 @@ __device__ void copy_new_rows(const MqParams& P, uint32_t wg)
     }
 }
 
-template <int D, int B, bool kCascade, int QT>
+template <int D, int B, bool kCascade, int QT, bool kFp8>
 __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
 {
     constexpr int N = kMqChunk;           // tokens per staged chunk
@@ -255,7 +274,11 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     const int lp = tid % DG, lq = tid / DG;
     const int64_t block_elems = (int64_t)B * P.num_heads * D;
     const int token_stride = P.num_heads * D;
-    u32x4 kr[4], vr[4];
+    typedef typename Raw8<kFp8>::type Raw;
+    constexpr int EB = kFp8 ? 1 : 2;  // bytes per cache element
+    const char* k_bytes = static_cast<const char*>(P.k_cache);
+    const char* v_bytes = static_cast<const char*>(P.v_cache);
+    Raw kr[4], vr[4];
     // The physical block of this thread's four tokens of the chunk at t0 (one
     // block, as 4 divides B).  Loaded a chunk ahead of its K/V loads, so that
     // their addresses never wait on a table read.  The position is clamped
@@ -276,17 +299,17 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
         if (t + 4 <= stream_end) {  // all four tokens exist: no selects
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t e = base + (int64_t)j * token_stride;
-                kr[j] = *reinterpret_cast<const u32x4*>(P.k_cache + e);
-                vr[j] = *reinterpret_cast<const u32x4*>(P.v_cache + e);
+                const int64_t e = (base + (int64_t)j * token_stride) * EB;
+                kr[j] = *reinterpret_cast<const Raw*>(k_bytes + e);
+                vr[j] = *reinterpret_cast<const Raw*>(v_bytes + e);
             }
         } else {  // the stream ends inside this group: zeros past the end
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool ok = t + j < stream_end;
-                const int64_t e = base + (int64_t)j * token_stride;
-                kr[j] = ok ? *reinterpret_cast<const u32x4*>(P.k_cache + e) : u32x4{0, 0, 0, 0};
-                vr[j] = ok ? *reinterpret_cast<const u32x4*>(P.v_cache + e) : u32x4{0, 0, 0, 0};
+                const int64_t e = (base + (int64_t)j * token_stride) * EB;
+                kr[j] = ok ? *reinterpret_cast<const Raw*>(k_bytes + e) : Raw{};
+                vr[j] = ok ? *reinterpret_cast<const Raw*>(v_bytes + e) : Raw{};
             }
         }
     };
@@ -308,8 +331,8 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
         if (loader) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                *reinterpret_cast<u32x4*>(&ks[(4 * lq + j) * KS + 8 * lp]) = kr[j];
-                *reinterpret_cast<u32x4*>(&vs[(4 * lq + j) * VS + 8 * lp]) = vr[j];
+                *reinterpret_cast<u32x4*>(&ks[(4 * lq + j) * KS + 8 * lp]) = widen8(kr[j]);
+                *reinterpret_cast<u32x4*>(&vs[(4 * lq + j) * VS + 8 * lp]) = widen8(vr[j]);
             }
         }
         if (t0 + N < stream_end)
@@ -429,7 +452,8 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
         const int r = wr0 + 16 * qt + c;
         if (r >= n_rows)
             continue;
-        const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+        // FP8: the V scale (the K scale is in scale_log2)
+        const float inv = (lsum > 0.0f ? 1.0f / lsum : 0.0f) * (kFp8 ? P.v_scale : 1.0f);
         if constexpr (kCascade) {
             const int64_t u = ((row0 + r) * P.num_heads + h) * P.num_slots + part;
 #pragma unroll
@@ -454,19 +478,19 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     }
 }
 
-template <bool kCascade>
+template <bool kCascade, bool kFp8>
 hipError_t launch_mq(const MqParams& P, int head_dim, int block_size, hipStream_t stream)
 {
     constexpr int QT = (kCascade ? kCascadeTileRows : kMqTileRows) / (kWaves * 16);
     const dim3 grid(P.total_units + (kCascade ? P.copy_units : 0u)), block(kMqThreads);
     if (head_dim == 128 && block_size == 16)
-        hipLaunchKernelGGL((pa_mq_kernel<128, 16, kCascade, QT>), grid, block, 0, stream, P);
+        hipLaunchKernelGGL((pa_mq_kernel<128, 16, kCascade, QT, kFp8>), grid, block, 0, stream, P);
     else if (head_dim == 128 && block_size == 32)
-        hipLaunchKernelGGL((pa_mq_kernel<128, 32, kCascade, QT>), grid, block, 0, stream, P);
+        hipLaunchKernelGGL((pa_mq_kernel<128, 32, kCascade, QT, kFp8>), grid, block, 0, stream, P);
     else if (head_dim == 64 && block_size == 16)
-        hipLaunchKernelGGL((pa_mq_kernel<64, 16, kCascade, QT>), grid, block, 0, stream, P);
+        hipLaunchKernelGGL((pa_mq_kernel<64, 16, kCascade, QT, kFp8>), grid, block, 0, stream, P);
     else if (head_dim == 64 && block_size == 32)
-        hipLaunchKernelGGL((pa_mq_kernel<64, 32, kCascade, QT>), grid, block, 0, stream, P);
+        hipLaunchKernelGGL((pa_mq_kernel<64, 32, kCascade, QT, kFp8>), grid, block, 0, stream, P);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -476,13 +500,27 @@ hipError_t launch_mq(const MqParams& P, int head_dim, int block_size, hipStream_
 
 hipError_t launch_multiquery(const MqParams& p, int head_dim, int block_size, hipStream_t stream)
 {
-    return launch_mq<false>(p, head_dim, block_size, stream);
+    return launch_mq<false, false>(p, head_dim, block_size, stream);
+}
+
+hipError_t launch_multiquery_fp8(const MqParams& p, int head_dim, int block_size,
+                                 hipStream_t stream)
+{
+    return launch_mq<false, true>(p, head_dim, block_size, stream);
 }
 
 hipError_t launch_cascade_prefix(const MqParams& p, int head_dim, int block_size,
                                  hipStream_t stream)
 {
-    return launch_mq<true>(p, head_dim, block_size, stream);
+    return launch_mq<true, false>(p, head_dim, block_size, stream);
+}
+
+hipError_t launch_cascade_prefix_fp8(const MqParams& p, int head_dim, int block_size,
+                                     hipStream_t stream)
+{
+    if (p.new_k != nullptr)
+        return hipErrorInvalidValue;  // the appending form copies fp16 rows only
+    return launch_mq<true, true>(p, head_dim, block_size, stream);
 }
 
 }  // namespace pa

@@ -227,3 +227,42 @@ def test_cascade_append_rejects(lib):
     assert _cascade_append(lib, plen=0, D=96) == -3      # (decode checks before the write)
     assert _cascade_append(lib, plen=0, P=24) == -4
     assert _cascade_append(lib, S=0, out=P(0), key=P(0), sm=P(0)) == 0  # nothing to do
+
+
+def test_cascade_fp8_rejects(lib):
+    # every call below must fail validation (or have nothing to do): the pointers are fake
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, pt=FAKE, plen=64, bt=FAKE, cl=FAKE, S=2, H=4,
+                 D=128, NB=8, B=16, MB=4, scale=0.088, ks=0.01, vs=0.01, P=0, ws=FAKE,
+                 wsb=1 << 30)
+        a.update(kw)
+        return lib.pa_decode_cascade_fp8(a["out"], a["q"], a["k"], a["v"], a["pt"], a["plen"],
+                                         a["bt"], a["cl"], a["S"], a["H"], a["D"], a["NB"],
+                                         a["B"], a["MB"], a["scale"], a["ks"], a["vs"], a["P"],
+                                         a["ws"], a["wsb"], None)
+    assert call(ks=0.0) == -2
+    assert call(vs=float("nan")) == -2
+    assert call(plen=17) == -2
+    assert call(D=96) == -3
+    assert call(P=24) == -4
+    assert call(wsb=16) == -5
+    assert call(pt=P(0)) == -1
+    assert call(plen=0, D=96) == -3       # no prefix: pa_decode_fp8's checks
+    assert call(S=0, out=P(0)) == 0
+
+
+def test_multi_query_fp8_rejects(lib):
+    # every call below must fail validation (or have nothing to do): the pointers are fake
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, S=2, T=10, maxq=8,
+                 H=4, D=128, NB=8, B=16, MB=4, scale=0.088, ks=0.01, vs=0.01)
+        a.update(kw)
+        return lib.pa_multi_query_fp8(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"],
+                                      a["S"], a["T"], a["maxq"], a["H"], a["D"], a["NB"], a["B"],
+                                      a["MB"], a["scale"], a["ks"], a["vs"], None)
+    assert call(ks=-1.0) == -2
+    assert call(vs=float("inf")) == -2
+    assert call(D=96) == -3
+    assert call(qs=P(0)) == -1
+    assert call(q=P(0x10004)) == -6
+    assert call(S=0, out=P(0)) == 0
