@@ -373,7 +373,8 @@ def bench_cascade(iters, warmup, cpu=None, fp8=False):
                      "kernel": ("pa_decode_cascade_fp8" if fp8 else "pa_decode_cascade")
                                + " (prefix pass + partition kernel): HIP events around calls "
                                "back to back",
-                     "traffic": None if fp8 else _traffic("cascade_config3_B16_P0", "cascade")},
+                     "traffic": _traffic(("fp8_" if fp8 else "") + "cascade_config3_B16_P0",
+                                         "cascade")},
         "logical_kv_gbs": round(logical / (dec * 1e-3) / 1e9, 1),
         "cpu_baseline": line_cpu}), flush=True)
 
@@ -441,8 +442,8 @@ def bench_multi_query(iters, warmup, cpu=None, fp8=False):
         "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 2),
                      "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / t / 1e12 / MFMA_F16_TFLOPS, 4),
-                     "traffic": None if fp8 else _traffic("multi_query_16x2048_last512",
-                                                          "multi_query")},
+                     "traffic": _traffic(("fp8_" if fp8 else "") + "multi_query_16x2048_last512",
+                                         "multi_query")},
         "kv_unique_gbs": round(kv_unique / t / 1e9, 1), "cpu_baseline": line_cpu}), flush=True)
 
 
