@@ -241,8 +241,7 @@ def bench_cascade(iters, warmup, cpu=None, fp8=False):
     """Shared-prefix step (config 3) with the prefix read once per 64
     sequences: pa_decode_cascade_append (the new tokens are written by the
     prefix pass's launch); the same step as two calls (reshape_and_cache +
-    pa_decode_cascade) is reported beside it.  FP8 caches: the two calls
-    reshape_and_cache_fp8 + pa_decode_cascade_fp8 are the step."""
+    pa_decode_cascade) is reported beside it.  FP8 caches: the _fp8 forms."""
     import numpy as np
     import torch
     import paged_kv_cache_155_amd as pa
@@ -280,9 +279,9 @@ def bench_cascade(iters, warmup, cpu=None, fp8=False):
             pa.decode_cascade(out, q, kc, vc, pt, plen, stt, slt, scale, P, ws)
 
     def step():
-        if fp8:  # no one-call form over FP8 caches
-            reshape()
-            decode()
+        if fp8:
+            pa.decode_cascade_append_fp8(out, q, key, val, kc, vc, slots, pt, plen, stt, slt,
+                                         scale, f8.k_scale, f8.v_scale, P, ws)
         else:
             pa.decode_cascade_append(out, q, key, val, kc, vc, slots, pt, plen, stt, slt, scale,
                                      P, ws)
@@ -361,8 +360,7 @@ def bench_cascade(iters, warmup, cpu=None, fp8=False):
         "t_decode_us_events_mean": round(dec_events * 1e3, 2),
         "t_reshape_us_mean": round(rc * 1e3, 2),
         "wall_ms_per_step": round(step_ms, 4), "ms_per_step": round(step_gpu, 6),
-        "step": ("reshape_and_cache_fp8 + pa_decode_cascade_fp8" if fp8
-                 else "pa_decode_cascade_append"),
+        "step": "pa_decode_cascade_append" + ("_fp8" if fp8 else ""),
         "ms_per_step_two_calls": round(step_two, 6),
         "decode_tokens_per_s_per_layer": round(w.num_seqs / (step_gpu * 1e-3), 1),
         "kv_bytes_logical": logical, "kv_bytes_unique": uniq,

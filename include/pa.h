@@ -285,6 +285,23 @@ int pa_decode_cascade_fp8(void* out, const void* q, const void* k_cache, const v
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_cascade_append over FP8 caches: the same arguments and
+ * semantics, with k_scale / v_scale as in pa_decode_cascade_fp8; the new
+ * rows (fp16) are quantised exactly as pa_reshape_and_cache_fp8 quantises
+ * them.  Under the same precondition, out and both caches are bitwise what
+ * pa_reshape_and_cache_fp8 followed by pa_decode_cascade_fp8 produce.
+ */
+int pa_decode_cascade_append_fp8(void* out, const void* q, const void* key, const void* value,
+                                 void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                 const int32_t* prefix_block_table, int32_t prefix_len,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t num_blocks, int32_t block_size,
+                                 int32_t max_blocks_per_seq, float scale, float k_scale,
+                                 float v_scale, int32_t partition_size, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * pa_multi_query over FP8 caches: the same arguments, semantics and errors as
  * pa_multi_query, with k_cache / v_cache holding E4M3 codes dequantised as in
  * pa_decode_fp8 (k_scale, v_scale finite and > 0, else PA_ERR_INVALID_DIM).

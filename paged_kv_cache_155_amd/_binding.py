@@ -62,6 +62,10 @@ def load(path=None):
                                           + [ctypes.c_float] * 3
                                           + [_I32, _P, ctypes.c_size_t, _P])
     lib.pa_decode_cascade_fp8.restype = ctypes.c_int
+    lib.pa_decode_cascade_append_fp8.argtypes = ([_P] * 8 + [_I32] + [_P] * 2 + [_I32] * 6
+                                                 + [ctypes.c_float] * 3
+                                                 + [_I32, _P, ctypes.c_size_t, _P])
+    lib.pa_decode_cascade_append_fp8.restype = ctypes.c_int
     lib.pa_multi_query.argtypes = [_P] * 7 + [_I32] * 8 + [ctypes.c_float, _P]
     lib.pa_multi_query.restype = ctypes.c_int
     lib.pa_multi_query_fp8.argtypes = [_P] * 7 + [_I32] * 8 + [ctypes.c_float] * 3 + [_P]
@@ -348,6 +352,42 @@ def decode_cascade_fp8(out, q, k_cache, v_cache, prefix_table, prefix_len, block
                                       _ptr(workspace), workspace.numel(), _stream_ptr(stream))
     if rc != PA_OK:
         raise PAError(rc, "pa_decode_cascade_fp8")
+    return out
+
+
+def decode_cascade_append_fp8(out, q, key, value, k_cache, v_cache, slot_mapping, prefix_table,
+                              prefix_len, block_tables, context_lens, scale, k_scale, v_scale,
+                              partition_size=512, workspace=None, stream=None):
+    """decode_cascade_append() over FP8 caches: the new rows are quantised as
+    reshape_and_cache_fp8 quantises them (values = code * scale)."""
+    import torch
+    _check_fp8_cache(k_cache, "k_cache")
+    NB, B, H, D = k_cache.shape
+    _check_fp8_cache(v_cache, "v_cache", shape=k_cache.shape)
+    _check(q, "q", torch.float16, ndim=3)
+    S = q.shape[0]
+    _check(q, "q", torch.float16, shape=(S, H, D))
+    _check(out, "out", torch.float16, shape=(S, H, D))
+    _check_new_tokens(key, value, slot_mapping, S, H, D)
+    _check(prefix_table, "prefix_table", torch.int32, ndim=1)
+    if prefix_len % B or prefix_table.numel() * B < prefix_len:
+        raise ValueError("prefix_len must be a multiple of the block size covered by prefix_table")
+    _check(block_tables, "block_tables", torch.int32, ndim=2)
+    MB = block_tables.shape[1]
+    _check(block_tables, "block_tables", torch.int32, shape=(S, MB))
+    _check(context_lens, "context_lens", torch.int32, shape=(S,))
+    need = decode_cascade_workspace_size(S, H, D, B, int(prefix_len), MB, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check(workspace, "workspace", torch.uint8, ndim=1)
+    rc = load().pa_decode_cascade_append_fp8(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+        _ptr(slot_mapping), _ptr(prefix_table), int(prefix_len), _ptr(block_tables),
+        _ptr(context_lens), S, H, D, NB, B, MB, float(scale), float(k_scale), float(v_scale),
+        int(partition_size), _ptr(workspace), workspace.numel(), _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_decode_cascade_append_fp8")
     return out
 
 

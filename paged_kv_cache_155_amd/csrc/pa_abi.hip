@@ -214,8 +214,8 @@ struct Fp8Scales {
     float k, v;
 };
 
-// pa_decode_cascade; pa_decode_cascade_append when append (fp16 only);
-// pa_decode_cascade_fp8 when fp8 != nullptr
+// pa_decode_cascade; pa_decode_cascade_append when append; the _fp8 forms
+// of both when fp8 != nullptr
 int cascade(void* out, const void* q, const void* key, const void* value, void* k_cache,
             void* v_cache, const int64_t* slot_mapping, const int32_t* prefix_block_table,
             int32_t prefix_len, const int32_t* block_tables, const int32_t* context_lens,
@@ -235,16 +235,16 @@ int cascade(void* out, const void* q, const void* key, const void* value, void* 
     if (append && num_seqs > 0 &&
         (!aligned16(key) || !aligned16(value) || (reinterpret_cast<uintptr_t>(slot_mapping) & 7u)))
         return PA_ERR_ALIGN;
-    if (prefix_len == 0 && fp8)  // nothing shared: the plain decode
-        return pa_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
-                             num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
-                             scale, fp8->k, fp8->v, partition_size, workspace, workspace_bytes,
-                             stream);
-    if (prefix_len == 0) {  // nothing shared: the plain step (its own write, then pa_decode)
+    if (prefix_len == 0) {  // nothing shared: the plain step (its own write, then the decode)
         if (!append)
-            return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
-                             num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
-                             scale, partition_size, workspace, workspace_bytes, stream);
+            return fp8 ? pa_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens,
+                                       num_seqs, num_heads, head_dim, num_blocks, block_size,
+                                       max_blocks_per_seq, scale, fp8->k, fp8->v,
+                                       partition_size, workspace, workspace_bytes, stream)
+                       : pa_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   num_seqs, num_heads, head_dim, num_blocks, block_size,
+                                   max_blocks_per_seq, scale, partition_size, workspace,
+                                   workspace_bytes, stream);
         pa::DecodeParams p;  // every decode check before the write is enqueued
         int rc = prepare_decode(p, out, q, k_cache, v_cache, block_tables, context_lens,
                                 num_seqs, num_heads, head_dim, num_blocks, block_size,
@@ -252,12 +252,21 @@ int cascade(void* out, const void* q, const void* key, const void* value, void* 
                                 workspace_bytes);
         if (rc != PA_OK)
             return rc == 1 ? PA_OK : rc;
-        rc = pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_seqs,
-                                  num_heads, head_dim, num_blocks, block_size, stream);
+        if (fp8) {
+            p.scale_log2 = (float)((double)scale * (double)fp8->k * 1.4426950408889634074);
+            p.v_scale = fp8->v;
+        }
+        rc = fp8 ? pa_reshape_and_cache_fp8(key, value, k_cache, v_cache, slot_mapping,
+                                            num_seqs, num_heads, head_dim, num_blocks,
+                                            block_size, fp8->k, fp8->v, stream)
+                 : pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_seqs,
+                                        num_heads, head_dim, num_blocks, block_size, stream);
         if (rc != PA_OK)
             return rc;  // its checks fail before it enqueues anything
-        hipError_t e = pa::launch_decode_dispatch(p, head_dim, block_size,
-                                                  static_cast<hipStream_t>(stream));
+        hipError_t e = fp8 ? pa::launch_decode_fp8_dispatch(p, head_dim, block_size,
+                                                             static_cast<hipStream_t>(stream))
+                           : pa::launch_decode_dispatch(p, head_dim, block_size,
+                                                        static_cast<hipStream_t>(stream));
         return e == hipSuccess ? PA_OK : PA_ERR_HIP;
     }
     if (head_dim != 64 && head_dim != 128)
@@ -299,8 +308,12 @@ int cascade(void* out, const void* q, const void* key, const void* value, void* 
     if (append) {  // the prefix pass also writes the new tokens (into private suffix slots)
         m.new_k = static_cast<const _Float16*>(key);
         m.new_v = static_cast<const _Float16*>(value);
-        m.k_store = static_cast<_Float16*>(k_cache);
-        m.v_store = static_cast<_Float16*>(v_cache);
+        m.k_store = k_cache;
+        m.v_store = v_cache;
+        if (fp8) {  // the cache-write quantiser multiplies by 1/scale rounded to float
+            m.k_inv = (float)(1.0 / (double)fp8->k);
+            m.v_inv = (float)(1.0 / (double)fp8->v);
+        }
         m.slot_mapping = slot_mapping;
         m.cache_slots = (int64_t)num_blocks * block_size;
         const int64_t copy_units = pa::copy_workgroups(m, head_dim);
@@ -350,6 +363,23 @@ int pa_decode_cascade_fp8(void* out, const void* q, const void* k_cache, const v
                    block_tables, context_lens, num_seqs, num_heads, head_dim, num_blocks,
                    block_size, max_blocks_per_seq, scale, partition_size, workspace,
                    workspace_bytes, stream, /*append=*/false, &sc);
+}
+
+int pa_decode_cascade_append_fp8(void* out, const void* q, const void* key, const void* value,
+                                 void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                 const int32_t* prefix_block_table, int32_t prefix_len,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t num_blocks, int32_t block_size,
+                                 int32_t max_blocks_per_seq, float scale, float k_scale,
+                                 float v_scale, int32_t partition_size, void* workspace,
+                                 size_t workspace_bytes, void* stream)
+{
+    const Fp8Scales sc{k_scale, v_scale};
+    return cascade(out, q, key, value, k_cache, v_cache, slot_mapping, prefix_block_table,
+                   prefix_len, block_tables, context_lens, num_seqs, num_heads, head_dim,
+                   num_blocks, block_size, max_blocks_per_seq, scale, partition_size, workspace,
+                   workspace_bytes, stream, /*append=*/true, &sc);
 }
 
 int pa_decode_cascade_append(void* out, const void* q, const void* key, const void* value,

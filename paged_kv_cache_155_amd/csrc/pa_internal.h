@@ -63,14 +63,16 @@ struct MqParams {
     float v_scale;                 // FP8: dequantisation scale of V
     uint32_t copy_units;           // shared prefix, appending form: copy workgroups first
     // shared prefix, appending form (new_k == nullptr otherwise): row s of
-    // new_k / new_v [S, H, D] goes to cache slot slot_mapping[s] when
-    // 0 <= slot < cache_slots (a private suffix slot, never a prefix block)
+    // new_k / new_v [S, H, D] (fp16) goes to cache slot slot_mapping[s] when
+    // 0 <= slot < cache_slots (a private suffix slot, never a prefix block);
+    // FP8 caches get the codes E4M3(x * k_inv) / E4M3(x * v_inv)
     const _Float16* new_k;
     const _Float16* new_v;
-    _Float16* k_store;             // the caches again, written through these
-    _Float16* v_store;
+    void* k_store;                 // the caches again, written through these
+    void* v_store;
     const int64_t* slot_mapping;
     int64_t cache_slots;           // num_blocks * block_size
+    float k_inv, v_inv;            // FP8: 1 / scale, rounded to float
 };
 
 hipError_t launch_multiquery(const MqParams& p, int head_dim, int block_size, hipStream_t stream);

@@ -47,6 +47,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_fp8_quant.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -140,9 +141,8 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n)
 // slots, 16 bytes of K and of V per item, kCopyItems items per thread with
 // every load (slot and data alike) issued before the first store.  The slots
 // are private suffix slots, so these writes never meet the prefix units'
-// reads.
-
-template <int D>
+// reads.  FP8 caches get the codes of the cache-write quantiser.
+template <int D, bool kFp8>
 __device__ void copy_new_rows(const MqParams& P, uint32_t wg)
 {
     constexpr int kPieces = D / 8;  // 16-byte pieces of a head row
@@ -167,8 +167,15 @@ __device__ void copy_new_rows(const MqParams& P, uint32_t wg)
 #pragma unroll
     for (int j = 0; j < kCopyItems; ++j) {
         if (dst[j] >= 0) {
-            *reinterpret_cast<u32x4*>(P.k_store + dst[j]) = kv[j];
-            *reinterpret_cast<u32x4*>(P.v_store + dst[j]) = vv[j];
+            if constexpr (kFp8) {  // one byte per element
+                *reinterpret_cast<u32x2*>(static_cast<char*>(P.k_store) + dst[j]) =
+                    fp8::quantize8(kv[j], P.k_inv);
+                *reinterpret_cast<u32x2*>(static_cast<char*>(P.v_store) + dst[j]) =
+                    fp8::quantize8(vv[j], P.v_inv);
+            } else {
+                *reinterpret_cast<u32x4*>(static_cast<_Float16*>(P.k_store) + dst[j]) = kv[j];
+                *reinterpret_cast<u32x4*>(static_cast<_Float16*>(P.v_store) + dst[j]) = vv[j];
+            }
         }
     }
 }
@@ -195,7 +202,7 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     uint32_t wg = blockIdx.x;
     if constexpr (kCascade) {
         if (wg < P.copy_units) {  // a copy workgroup (appending form only)
-            copy_new_rows<D>(P, wg);
+            copy_new_rows<D, kFp8>(P, wg);
             return;  // the whole workgroup, before any barrier
         }
         wg -= P.copy_units;  // a multiple of 8: the XCD of each prefix unit is kept
@@ -518,8 +525,6 @@ hipError_t launch_cascade_prefix(const MqParams& p, int head_dim, int block_size
 hipError_t launch_cascade_prefix_fp8(const MqParams& p, int head_dim, int block_size,
                                      hipStream_t stream)
 {
-    if (p.new_k != nullptr)
-        return hipErrorInvalidValue;  // the appending form copies fp16 rows only
     return launch_mq<true, true>(p, head_dim, block_size, stream);
 }
 

@@ -266,3 +266,23 @@ def test_multi_query_fp8_rejects(lib):
     assert call(qs=P(0)) == -1
     assert call(q=P(0x10004)) == -6
     assert call(S=0, out=P(0)) == 0
+
+
+def test_cascade_append_fp8_rejects(lib):
+    # every call below must fail validation (or have nothing to do): the pointers are fake
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, k=FAKE, v=FAKE, sm=FAKE, pt=FAKE,
+                 plen=64, bt=FAKE, cl=FAKE, S=2, H=4, D=128, NB=8, B=16, MB=4, scale=0.088,
+                 ks=0.01, vs=0.01, P=0, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.pa_decode_cascade_append_fp8(
+            a["out"], a["q"], a["key"], a["value"], a["k"], a["v"], a["sm"], a["pt"], a["plen"],
+            a["bt"], a["cl"], a["S"], a["H"], a["D"], a["NB"], a["B"], a["MB"], a["scale"],
+            a["ks"], a["vs"], a["P"], a["ws"], a["wsb"], None)
+    assert call(ks=0.0) == -2
+    assert call(key=P(0)) == -1
+    assert call(value=P(0x10008)) == -6
+    assert call(D=96) == -3
+    assert call(plen=0, D=96) == -3   # no prefix: decode checks before the write
+    assert call(plen=0, ks=-1.0) == -2
+    assert call(S=0, out=P(0), key=P(0), sm=P(0)) == 0
