@@ -217,3 +217,55 @@ def test_multi_query_fp8_chunked_prefill_batch(orc):
     got, ref = _mq_fp8(orc, w, q, qs, 256)
     ea, _ = assert_close(got, ref, "fp8 chunked prefill batch")
     log(f"[fp8] multi-query batch: max abs err {ea:.3e}")
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["fp16", "fp8"])
+def test_multi_query_graph_capture(orc, fp8):
+    """pa_multi_query(_fp8) enqueues one kernel and nothing else: captured in
+    a HIP graph and replayed three times (output reset between replays, eager
+    work and synchronisations in between), every replay is bitwise equal to
+    the eager call, which matches the oracle."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import fp8_pools, make_multi_query
+    w, q, qs = make_multi_query([300, 1000, 64, 129], [40, 300, 64, 1], 4, 128, 16, seed=12,
+                                poison=False)
+    log(f"[graph] multi-query {'fp8' if fp8 else 'fp16'}")
+    f = fp8_pools(w) if fp8 else None
+    kc = to_dev(f.k_cache if fp8 else w.k_cache)
+    vc = to_dev(f.v_cache if fp8 else w.v_cache)
+    qd, bt, cl, qsd = to_dev(q), to_dev(w.block_tables), to_dev(w.context_lens), to_dev(qs)
+
+    def call(out):
+        if fp8:
+            pa.multi_query_fp8(out, qd, kc, vc, bt, cl, qsd, 300, float(w.scale), f.k_scale,
+                               f.v_scale)
+        else:
+            pa.multi_query(out, qd, kc, vc, bt, cl, qsd, 300, float(w.scale))
+
+    eager = torch.full_like(qd, float("nan"))
+    call(eager)
+    torch.cuda.synchronize()
+    if fp8:
+        ref = orc.prefill_fp8(q, f.k_cache, f.v_cache, w.block_tables, w.context_lens, qs,
+                              float(w.scale), f.k_scale, f.v_scale)
+    else:
+        ref = orc.prefill(q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, qs,
+                          float(w.scale))
+    assert_close(eager.cpu().numpy(), ref, "eager multi-query")
+    out = torch.full_like(qd, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call(out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), eager.cpu().numpy().view(np.uint16)), \
+            f"replay {i} differs from the eager call"
