@@ -88,9 +88,17 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
 /*
  * Bytes of device workspace pa_decode needs for the split-context path:
  * fp32 partial results (output row, running maximum, running sum) for each
- * (sequence, head, context partition).  Returns 0 when no split happens
- * (partition_size == 0, or a single partition covers max_blocks_per_seq *
- * block_size tokens) and 0 for invalid arguments.
+ * (sequence, head, context partition).  [src] §六 names a second version of
+ * PagedAttention ("v2") without describing it; the split reading here is
+ * partitions of partition_size logical tokens starting at multiples of it,
+ * each reduced to (max, sum, normalised row) and merged by the exact
+ * log-sum-exp identity of the softmax in [10x] §2.1.  Layout in the
+ * workspace: o [num_seqs, num_heads, NP, head_dim], then m and l
+ * [num_seqs, num_heads, NP], each part starting at a 256-byte boundary,
+ * NP = ceil(max_blocks_per_seq * block_size / partition_size).  Returns 0
+ * when no split happens (partition_size == 0, or a single partition covers
+ * max_blocks_per_seq * block_size tokens) and 0 for invalid arguments (no
+ * error code: pa_decode reports those).  Host only; no device call.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t block_size, int32_t max_blocks_per_seq,
@@ -360,7 +368,13 @@ int pa_swap_blocks(const void* src, void* dst, const int64_t* block_mapping, int
                    int32_t src_num_blocks, int32_t dst_num_blocks, int64_t block_bytes,
                    void* stream);
 
-/* Static description of a status code (never NULL). */
+/*
+ * Static text of a status code returned by any entry point above (never
+ * NULL; an unknown code gives "unknown pa status").  The codes and the
+ * conditions behind them are this library's own (the pages define no error
+ * interface; [eng] §3.3 only has the block manager raise when no block is
+ * free).  The string is owned by the library and must not be freed.
+ */
 const char* pa_status_string(int status);
 
 #ifdef __cplusplus

@@ -23,5 +23,24 @@ def build(src=SRC, out=LIB, extra_flags=(), quiet=False):
     return out
 
 
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source: any
+# out-of-bounds access, use after free or undefined operation aborts.
+SANITIZE_FLAGS = ("-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g")
+
+
+def build_sanitized(out, src=SRC, quiet=True):
+    """The oracle with ASan/UBSan (host code only; gcc, no GPU code)."""
+    return build(src, out, extra_flags=SANITIZE_FLAGS, quiet=quiet)
+
+
+def sanitizer_preload():
+    """The runtime a non-instrumented python must preload to load an ASan
+    library (ASan has to come first in the process)."""
+    r = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                       check=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
     build(quiet="-q" in sys.argv)

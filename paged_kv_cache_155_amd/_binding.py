@@ -36,6 +36,12 @@ def load(path=None):
         raise ImportError(
             f"HIP library not built: {p} is missing (build it with "
             f"`python -m paged_kv_cache_155_amd._build` or __graft_entry__.build())")
+    # torch ships its own HIP runtime (torch/lib/libamdhip64.so).  libpa.so
+    # must bind to that one: loaded before torch, it would pull in the system
+    # runtime as well, and its launches could not use torch's memory and
+    # streams.  With torch loaded, libpa.so's libamdhip64.so.7 dependency
+    # resolves to the runtime already in the process.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     lib.pa_reshape_and_cache.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P]
     lib.pa_reshape_and_cache.restype = ctypes.c_int
@@ -111,6 +117,18 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _alloc_workspace(nbytes, device, stream):
+    """A uint8 workspace for kernels launched on `stream` (None: the current
+    stream).  It is allocated while that stream is current, so when the
+    tensor is released the caching allocator hands its memory only to work
+    ordered after these kernels on the same stream."""
+    import torch
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     """Write key/value [T, H, D] fp16 into k_cache/v_cache [NB, B, H, D] at
     slot_mapping [T] int64 (slot = block * B + offset; out-of-range slots,
@@ -158,7 +176,7 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, partitio
     _check(context_lens, "context_lens", torch.int32, shape=(S,))
     need = decode_workspace_size(S, H, D, B, MB, partition_size)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if need else None
+        workspace = _alloc_workspace(need, q.device, stream) if need else None
     elif need:
         _check(workspace, "workspace", torch.uint8, ndim=1)
     wbytes = workspace.numel() if workspace is not None else 0
@@ -265,7 +283,7 @@ def decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_sc
     _check(context_lens, "context_lens", torch.int32, shape=(S,))
     need = decode_workspace_size(S, H, D, B, MB, partition_size)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if need else None
+        workspace = _alloc_workspace(need, q.device, stream) if need else None
     elif need:
         _check(workspace, "workspace", torch.uint8, ndim=1)
     wbytes = workspace.numel() if workspace is not None else 0
@@ -308,7 +326,7 @@ def decode_cascade(out, q, k_cache, v_cache, prefix_table, prefix_len, block_tab
     _check(context_lens, "context_lens", torch.int32, shape=(S,))
     need = decode_cascade_workspace_size(S, H, D, B, int(prefix_len), MB, partition_size)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _alloc_workspace(max(need, 1), q.device, stream)
     else:
         _check(workspace, "workspace", torch.uint8, ndim=1)
     rc = load().pa_decode_cascade(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -342,7 +360,7 @@ def decode_cascade_fp8(out, q, k_cache, v_cache, prefix_table, prefix_len, block
     _check(context_lens, "context_lens", torch.int32, shape=(S,))
     need = decode_cascade_workspace_size(S, H, D, B, int(prefix_len), MB, partition_size)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _alloc_workspace(max(need, 1), q.device, stream)
     else:
         _check(workspace, "workspace", torch.uint8, ndim=1)
     rc = load().pa_decode_cascade_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -378,7 +396,7 @@ def decode_cascade_append_fp8(out, q, key, value, k_cache, v_cache, slot_mapping
     _check(context_lens, "context_lens", torch.int32, shape=(S,))
     need = decode_cascade_workspace_size(S, H, D, B, int(prefix_len), MB, partition_size)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _alloc_workspace(max(need, 1), q.device, stream)
     else:
         _check(workspace, "workspace", torch.uint8, ndim=1)
     rc = load().pa_decode_cascade_append_fp8(
@@ -416,7 +434,7 @@ def decode_cascade_append(out, q, key, value, k_cache, v_cache, slot_mapping, pr
     _check(context_lens, "context_lens", torch.int32, shape=(S,))
     need = decode_cascade_workspace_size(S, H, D, B, int(prefix_len), MB, partition_size)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _alloc_workspace(max(need, 1), q.device, stream)
     else:
         _check(workspace, "workspace", torch.uint8, ndim=1)
     rc = load().pa_decode_cascade_append(_ptr(out), _ptr(q), _ptr(key), _ptr(value),

@@ -286,3 +286,19 @@ def test_cascade_append_fp8_rejects(lib):
     assert call(plen=0, D=96) == -3   # no prefix: decode checks before the write
     assert call(plen=0, ks=-1.0) == -2
     assert call(S=0, out=P(0), key=P(0), sm=P(0)) == 0
+
+
+def test_one_hip_runtime_in_the_process():
+    """Loading the library before anything imports torch must not bring a
+    second HIP runtime into the process (torch ships its own libamdhip64; a
+    library bound to another copy cannot launch on torch's memory and
+    streams).  Checked in a fresh interpreter."""
+    import subprocess
+    import sys
+    code = ("import paged_kv_cache_155_amd as pa; pa.load(); import torch; "
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') "
+            "if 'libamdhip64' in l and 'x' in l.split()[1]}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip() == "1", r.stdout

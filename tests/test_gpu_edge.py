@@ -286,3 +286,36 @@ def test_odd_shapes(orc, S, H, D, B, lens, P):
     log(f"[edge] odd shape S={S} H={H} D={D} B={B} P={P} lens={lens}")
     w = make_random(lens, H, D, B, seed=S * 100 + H + D + B + P, partition_size=P)
     _parity(orc, w, P, f"odd shape S={S} H={H} D={D} B={B} P={P}")
+
+
+def test_binding_workspace_follows_explicit_stream(orc):
+    """decode(..., stream=s) with no workspace given: the binding allocates the
+    workspace for stream s, so memory allocated and overwritten on the current
+    stream right after each call (while s may still be running) is never the
+    partials' memory.  Every output matches the oracle."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import make_workload
+    log("[edge] binding workspace on an explicit stream")
+    w = make_workload(4, num_seqs=2, num_heads=8)  # 64 partitions per (sequence, head)
+    d = DeviceWorkload(w)
+    d.reshape_and_cache()
+    need = pa.decode_workspace_size(w.num_seqs, w.num_heads, w.head_dim, w.block_size,
+                                    w.max_blocks_per_seq, 512)
+    assert need > 0
+    torch.cuda.synchronize()
+    _, _, ref = oracle_after_write(orc, w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs, junk = [], []
+    for _ in range(4):
+        out = torch.empty_like(d.q)
+        pa.decode(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                  float(w.scale), partition_size=512, stream=s)
+        j = torch.empty(need, dtype=torch.uint8, device="cuda")  # current stream
+        j.fill_(0xFF)  # NaN as float32, were it the partials' memory
+        junk.append(j)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for i, out in enumerate(outs):
+        assert_close(out.cpu().numpy(), ref, f"call {i} on an explicit stream")

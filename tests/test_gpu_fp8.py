@@ -87,7 +87,7 @@ def test_every_code_decodes_exactly():
 SMALL = [(0, None, {}), (1, None, dict(num_seqs=16, num_heads=4)),
          (2, 32, dict(num_seqs=24, num_heads=3)), (3, None, dict(num_seqs=12, num_heads=2)),
          (4, None, dict(num_seqs=2, num_heads=2))]
-FULL = [(1, None, {}), (2, 16, {}), (3, None, {}), (4, None, {})]
+FULL = [(1, None, {}), (2, 16, {}), (2, 32, {}), (3, None, {}), (4, None, {})]
 
 
 @pytest.mark.parametrize("cfg,bs,kw", SMALL + FULL,

@@ -153,6 +153,51 @@ def test_cascade_suffix_edges(orc, prefix_blocks, B, D):
         assert_close(out.cpu().numpy(), ref, f"cascade edges P={P}")
 
 
+@pytest.mark.parametrize("P", [0, 512])
+def test_cascade_needles_and_late_outliers_full(orc, P):
+    """Full config 3 through pa_decode_cascade with keys that stress the
+    matrix-core prefix pass (fp16 weights in its P.V product) and the merge:
+    needle keys (24 x a unit query of some sequence) at the prefix's chunk
+    and piece boundaries, and keys 30x larger at a few late prefix positions
+    and late in every suffix long enough.  Elementwise against the oracle."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import make_workload, split_shared_prefix
+    w = make_workload(3)
+    log(f"[cascade] needles + late x30 outliers, full config 3, P={P}")
+    B, D = w.block_size, w.head_dim
+    kc = w.k_cache.copy()
+    pref = w.block_tables[0, :512 // B]
+    for j, pos in enumerate([0, 63, 64, 127, 128, 255, 256, 383, 384, 511]):
+        s = (7 * j + 3) % w.num_seqs
+        qv = w.q[s].astype(np.float32)  # [H, D]
+        kc[pref[pos // B], pos % B] = (24.0 * qv / np.linalg.norm(qv, axis=1, keepdims=True)
+                                       ).astype(np.float16)
+    rng = np.random.default_rng(303)
+
+    def boost(blk, off):
+        kc[blk, off] = (kc[blk, off].astype(np.float32) * 30.0).astype(np.float16)
+    for pos in rng.integers(400, 512, size=3):
+        boost(pref[pos // B], pos % B)
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        lo = 512 + (L - 512) // 2
+        if L - 1 > lo:  # never the new token's position L - 1
+            for pos in rng.integers(lo, L - 1, size=2):
+                boost(w.block_tables[s, pos // B], pos % B)
+    w.k_cache = kc
+    d = DeviceWorkload(w)
+    d.reshape_and_cache()
+    prefix, plen, suf_tables, suf_lens = split_shared_prefix(w, 512 // B)
+    out = torch.full_like(d.q, float("nan"))
+    pa.decode_cascade(out, d.q, d.k_cache, d.v_cache, to_dev(prefix), plen, to_dev(suf_tables),
+                      to_dev(suf_lens), float(w.scale), partition_size=P)
+    torch.cuda.synchronize()
+    _, _, ref = oracle_after_write(orc, w)
+    ea, er = assert_close(out.cpu().numpy(), ref, f"cascade needles/outliers P={P}")
+    log(f"[cascade] needles/outliers P={P}: max abs err {ea:.3e}, max rel err {er:.3e}")
+
+
 def test_cascade_repeated_calls_and_determinism(orc):
     """Calls on one workspace must not read the previous call's prefix
     pieces: three calls with different queries, each checked against the

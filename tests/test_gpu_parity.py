@@ -1,8 +1,10 @@
 """Parity of the HIP path with the CPU oracle on the five decode workloads.
 
 For each workload: pa_reshape_and_cache writes the step's new tokens, then
-pa_decode runs in the launch configuration the benchmark times (partition
-size 512).  The oracle does the same on the same host bytes.
+pa_decode runs in the launch configuration the benchmark times, i.e. each
+workload's own partition size (config 0: 16, config 1: 512, config 2: 1024,
+config 3: 0 = no split, config 4: 512).  The oracle does the same on the
+same host bytes.
   * reshape_and_cache: the entire K and V pools must be bitwise equal (any
     stray or missing write fails);
   * decode: every output element within 2e-3 + 1e-2 |oracle|.
