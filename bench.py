@@ -1,29 +1,40 @@
 #!/usr/bin/env python3
-"""Benchmark of one paged-attention decode step on one MI355X.
+"""Benchmark of the paged-attention decode step on one MI355X.
 
 A step is the whole hot path for one layer: pa_reshape_and_cache writes the
 step's new token of every sequence into its slot, then pa_decode (partition
 kernel + log-sum-exp reduce) attends over the paged K/V.  Inputs are seeded
 synthetic tensors, already resident in HBM when the timed region starts.
 
-    python bench.py [--steps K] [--warmup W] [--config 1] [--block-size B]
-                    [--partition-size P] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config C [--block-size B]
+                    [--partition-size P]] [--kv-dtype fp16|fp8] [--no-flush]
+                    [--no-cpu-baseline]
 
-Prints ONE JSON line.  value = K/V bytes the decode must read per step
-(sum of context lengths x heads x head_dim x 2 tensors x 2 bytes) divided
-by the step time of K steps run back to back with nothing else on the
-stream, in GB/s; tokens/s/layer = sequences / step time.  roofline: the
-decode call's HIP-event duration (events around each call in a second pass
-of K steps, on the stream the library launches on) against the 8 TB/s HBM3E
-peak and the measured streaming-read peak.  cpu_baseline: the CPU oracle
-timed on a bounded sample of the same workload on the host cores.
+Prints ONE JSON line.  By default the headline is the largest single-GPU
+workload, the LLaMA-13B-shaped layer (config 2: 256 sequences x 40 heads x
+128, block size 16, 1024-token partitions), and `per_config` carries every
+configuration in the same run: configs 0, 1, 2 at block sizes 16 and 32, 3
+through pa_decode and through pa_decode_cascade (the shared prefix read once
+per 64 sequences), and 4; each with its decode time, tokens/s/layer, the
+fraction of the 8 TB/s HBM peak on its unique K/V bytes, and the median
+decode time after a 1 GiB write that evicts the L2s and the MALL.  --config
+measures one workload only.
 
-`--probe copy` instead runs a plain copy of known size (reshape_and_cache
+value = K/V bytes the decode must read per step (sum of context lengths x
+heads x head_dim x 2 tensors x 2 bytes) divided by the step time of K steps
+run back to back between two HIP events, in GB/s; tokens/s/layer =
+sequences / step time.  roofline: K decode calls back to back between two
+HIP events on the stream the library launches on, against the 8 TB/s HBM3E
+peak and the measured streaming-read peak; traffic: HBM bytes per launch from
+the committed counter runs (profiles/traffic.json) when they were taken on
+the current device code, with their source.  cpu_baseline: the CPU oracle
+timed on a bounded sample of the headline workload on the host cores.
+
+`--op cascade | multi_query | copy_blocks | swap` time the other entry
+points; `--probe copy` runs a plain copy of known size (reshape_and_cache
 over 1 GiB) for calibrating hardware byte counters; `--probe read` runs the
 streaming-read probe (read_probe.hip, built by __graft_entry__.build()) whose
 best rate is the achievable-peak figure the roofline also reports against.
-`--flush` evicts the L2s and the MALL (a 1 GiB write) before every timed step
-and times the steps by HIP events instead.
 """
 import argparse
 import hashlib
@@ -43,10 +54,12 @@ METRIC = "paged-attn decode KV-read GB/s (fraction of HBM peak); decode tokens/s
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100,
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20,
                     help="untimed steps first (the GPU's clocks settle within some 20 ms)")
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=None,
+                    help="one workload only; default: config 2 (B 16) as the headline, with "
+                         "every configuration in per_config")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--kv-dtype", choices=["fp16", "fp8"], default="fp16",
@@ -66,8 +79,9 @@ def _args():
                          "3); multi_query: a chunked-prefill batch through pa_multi_query")
     ap.add_argument("--pairs", type=int, default=1024, help="blocks per copy/swap call")
     ap.add_argument("--probe", choices=["copy", "read"], default=None)
-    ap.add_argument("--flush", action="store_true",
-                    help="write 1 GiB before each timed step (evicts L2 and MALL)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the flushed decode timings (a 1 GiB write before each call "
+                         "evicts the L2s and the MALL)")
     ap.add_argument("--probe-mib", type=int, default=1024)
     return ap.parse_args()
 
@@ -87,26 +101,42 @@ def _code_sha(*paths):
 
 
 CSRC = os.path.join(ROOT, "paged_kv_cache_155_amd", "csrc")
-# sources whose code the counters of each kind of call were taken on
-TRAFFIC_SOURCES = {"decode": ("pa_decode.hip",),
-                   "cascade": ("pa_decode.hip", "pa_multiquery.hip"),
-                   "multi_query": ("pa_multiquery.hip",)}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def _traffic(config_name, kind="decode"):
-    """Per-launch HBM bytes from committed counter runs, if they were taken
-    on the current kernel code (comments aside); else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
+def kernel_code_sha():
+    """Key of the library's device code: every csrc source and header
+    (comments aside) and the compiler flags.  Counters recorded under another
+    key were taken on other code and are not reported."""
+    import glob
+    from paged_kv_cache_155_amd import _build
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
+                  + [os.path.join(ROOT, "include", "pa.h")])
+    return hashlib.sha256((_code_sha(*srcs) + " ".join(_build.FLAGS)).encode()).hexdigest()[:16]
+
+
+def _traffic(config_name):
+    """(per-launch HBM bytes, source) from the committed counter runs in
+    profiles/traffic.json, if they were taken on the current device code;
+    else (None, reason)."""
+    if not os.path.exists(TRAFFIC_JSON):
+        return None, "no profiles/traffic.json"
     try:
-        rec = json.load(open(path)).get(config_name)
+        rec = json.load(open(TRAFFIC_JSON)).get(config_name)
     except (ValueError, AttributeError):
-        return None
-    srcs = [os.path.join(CSRC, f) for f in TRAFFIC_SOURCES[kind]]
-    if not rec or rec.get("kernel_code_sha") != _code_sha(*srcs):
-        return None
-    return rec.get("bytes_per_launch")
+        return None, "unreadable profiles/traffic.json"
+    if not rec:
+        return None, f"no counters for {config_name} in profiles/traffic.json"
+    sha = kernel_code_sha()
+    if rec.get("kernel_code_sha") != sha:
+        return None, (f"profiles/traffic.json[{config_name}] was taken on code "
+                      f"{rec.get('kernel_code_sha')}, current {sha}")
+    return rec.get("bytes_per_launch"), f"profiles/traffic.json[{config_name}]@{sha}"
+
+
+def _traffic_fields(config_name):
+    b, src = _traffic(config_name)
+    return {"traffic": b, "traffic_source": src}
 
 
 def probe_copy(mib):
@@ -371,8 +401,7 @@ def bench_cascade(iters, warmup, cpu=None, fp8=False):
                      "kernel": ("pa_decode_cascade_fp8" if fp8 else "pa_decode_cascade")
                                + " (prefix pass + partition kernel): HIP events around calls "
                                "back to back",
-                     "traffic": _traffic(("fp8_" if fp8 else "") + "cascade_config3_B16_P0",
-                                         "cascade")},
+                     **_traffic_fields(("fp8_" if fp8 else "") + "cascade_config3_B16_P0")},
         "logical_kv_gbs": round(logical / (dec * 1e-3) / 1e9, 1),
         "cpu_baseline": line_cpu}), flush=True)
 
@@ -440,8 +469,7 @@ def bench_multi_query(iters, warmup, cpu=None, fp8=False):
         "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 2),
                      "peak": MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / t / 1e12 / MFMA_F16_TFLOPS, 4),
-                     "traffic": _traffic(("fp8_" if fp8 else "") + "multi_query_16x2048_last512",
-                                         "multi_query")},
+                     **_traffic_fields(("fp8_" if fp8 else "") + "multi_query_16x2048_last512")},
         "kv_unique_gbs": round(kv_unique / t / 1e9, 1), "cpu_baseline": line_cpu}), flush=True)
 
 
@@ -554,6 +582,213 @@ def cpu_baseline(w, sample_tokens, repeats, seconds, f8=None):
                       f"tokens/s/layer-equivalent {len(chosen) / H / dt:.1f}"}
 
 
+def _decode_calls(w, fp8, P):
+    """Upload one workload and return the step's two callables:
+    write() = reshape_and_cache(_fp8) of the step's new tokens, attend() =
+    decode(_fp8) over the paged K/V.  Inputs stay resident in HBM."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_155_amd as pa
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    if fp8:
+        from paged_kv_cache_155_amd.workloads import fp8_pools
+        f8 = fp8_pools(w)
+        kc, vc = up(f8.k_cache), up(f8.v_cache)
+        ks, vs = float(f8.k_scale), float(f8.v_scale)
+    else:
+        f8 = None
+        kc, vc = up(w.k_cache), up(w.v_cache)
+    q = up(w.q)
+    bt, cl = up(w.block_tables), up(w.context_lens)
+    key, val, slots = up(w.key), up(w.value), up(w.slot_mapping)
+    out = torch.empty_like(q)
+    need = pa.decode_workspace_size(w.num_seqs, w.num_heads, w.head_dim, w.block_size,
+                                    w.max_blocks_per_seq, P)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    scale = float(w.scale)
+
+    def write():
+        if fp8:
+            pa.reshape_and_cache_fp8(key, val, kc, vc, slots, ks, vs)
+        else:
+            pa.reshape_and_cache(key, val, kc, vc, slots)
+
+    def attend():
+        if fp8:
+            pa.decode_fp8(out, q, kc, vc, bt, cl, scale, ks, vs, partition_size=P, workspace=ws)
+        else:
+            pa.decode(out, q, kc, vc, bt, cl, scale, partition_size=P, workspace=ws)
+    return write, attend, f8
+
+
+def _cascade_calls(w, fp8):
+    """Config 3 through the shared-prefix entry points: write() + attend() is
+    reshape_and_cache + pa_decode_cascade; fused() is the same step as one
+    pa_decode_cascade_append call."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import fp8_pools, split_shared_prefix
+    prefix, plen, st, sl = split_shared_prefix(w, 512 // w.block_size)
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    f8 = fp8_pools(w) if fp8 else None
+    kc, vc = (up(f8.k_cache), up(f8.v_cache)) if fp8 else (up(w.k_cache), up(w.v_cache))
+    q = up(w.q)
+    key, val, slots = up(w.key), up(w.value), up(w.slot_mapping)
+    pt, stt, slt = up(prefix), up(st), up(sl)
+    out = torch.empty_like(q)
+    P = 0
+    ws = torch.empty(pa.decode_cascade_workspace_size(w.num_seqs, w.num_heads, w.head_dim,
+                                                      w.block_size, plen, st.shape[1], P),
+                     dtype=torch.uint8, device="cuda")
+    scale = float(w.scale)
+
+    def write():
+        if fp8:
+            pa.reshape_and_cache_fp8(key, val, kc, vc, slots, f8.k_scale, f8.v_scale)
+        else:
+            pa.reshape_and_cache(key, val, kc, vc, slots)
+
+    def attend():
+        if fp8:
+            pa.decode_cascade_fp8(out, q, kc, vc, pt, plen, stt, slt, scale, f8.k_scale,
+                                  f8.v_scale, P, ws)
+        else:
+            pa.decode_cascade(out, q, kc, vc, pt, plen, stt, slt, scale, P, ws)
+
+    def fused():
+        if fp8:
+            pa.decode_cascade_append_fp8(out, q, key, val, kc, vc, slots, pt, plen, stt, slt,
+                                         scale, f8.k_scale, f8.v_scale, P, ws)
+        else:
+            pa.decode_cascade_append(out, q, key, val, kc, vc, slots, pt, plen, stt, slt, scale,
+                                     P, ws)
+    return write, attend, fused, f8
+
+
+def _b2b_ms(fn, n):
+    """Mean ms of n calls of fn back to back between two HIP events on the
+    current stream (the one the library launches on)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def measure(write, attend, K, W, flush_iters, scratch, fused=None):
+    """Timings of one workload's step (write + attend):
+      t_step   K steps back to back (HIP events around the K steps);
+      t_decode K attend() calls back to back;
+      flushed  attend() after a 1 GiB write that evicts the L2s and the MALL,
+               HIP events around each call (median, p10, p90);
+      t_reshape mean of write() between events."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def step():
+        write()
+        attend()
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_step = _b2b_ms(step, K)
+    wall = time.perf_counter() - wall0
+    t_dec = _b2b_ms(attend, K)
+    t_fused = _b2b_ms(fused, K) if fused is not None else None
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for e in ev:
+        e[0].record(stream)
+        write()
+        e[1].record(stream)
+        attend()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    t_rc = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_dec_events = [e[1].elapsed_time(e[2]) for e in ev]
+    fl = []
+    if flush_iters:
+        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(flush_iters)]
+        for i, (a, b) in enumerate(fe):
+            scratch.fill_(i & 0xFF)
+            a.record(stream)
+            attend()
+            b.record(stream)
+        torch.cuda.synchronize()
+        fl = [a.elapsed_time(b) for a, b in fe]
+    r = {"t_step_ms": t_step, "t_decode_ms": t_dec, "t_reshape_ms": t_rc,
+         "t_decode_events_ms": t_dec_events, "t_decode_flushed_ms": fl, "wall_s": wall}
+    if t_fused is not None:
+        r["t_fused_step_ms"] = t_fused
+    return r
+
+
+SUITE = [  # (label, config, block size, call); partition size = the workload's own
+    ("config2_B16", 2, 16, "decode"),  # headline: the largest single-GPU workload
+    ("config0_B16", 0, None, "decode"),
+    ("config1_B16", 1, None, "decode"),
+    ("config2_B32", 2, 32, "decode"),
+    ("config3_B16", 3, None, "decode"),
+    ("config3_B16_cascade", 3, None, "cascade"),
+    ("config4_B16", 4, None, "decode"),
+]
+TARGET_FRAC = 0.70  # of the 8 TB/s HBM peak, on configs 1-4
+
+
+def _entry(label, cfg, w, call, fp8, r):
+    """One per_config record: times in us, rates on the workload's bytes."""
+    import numpy as np
+    eb = 1 if fp8 else 2
+    logical = w.kv_bytes() * eb // 2
+    uniq = w.unique_kv_bytes() * eb // 2
+    t_dec = r["t_decode_ms"] * 1e-3
+    step = r.get("t_fused_step_ms", r["t_step_ms"]) * 1e-3
+    fl = r["t_decode_flushed_ms"]
+    e = {"label": label, "config": cfg, "call": ("pa_decode_cascade" if call == "cascade"
+                                                 else "pa_decode") + ("_fp8" if fp8 else ""),
+         "block_size": w.block_size, "partition_size": 0 if call == "cascade" else w.partition_size,
+         "num_seqs": w.num_seqs, "num_heads": w.num_heads, "head_dim": w.head_dim,
+         "kv_bytes_logical": logical, "kv_bytes_unique": uniq,
+         "t_decode_us": round(t_dec * 1e6, 2),
+         "t_decode_us_events_median": round(float(np.median(r["t_decode_events_ms"])) * 1e3, 2),
+         "t_reshape_us": round(r["t_reshape_ms"] * 1e3, 2),
+         "t_step_us": round(step * 1e6, 2),
+         "step": ("pa_decode_cascade_append" + ("_fp8" if fp8 else "")) if call == "cascade"
+                 else "reshape_and_cache + pa_decode" + (" (fp8)" if fp8 else ""),
+         "decode_tokens_per_s_per_layer": round(w.num_seqs / step, 1),
+         "kv_gbs_unique": round(uniq / t_dec / 1e9, 1),
+         "frac": round(uniq / t_dec / 1e9 / HBM_PEAK_GBS, 4)}
+    if "t_fused_step_ms" in r:
+        e["t_step_two_calls_us"] = round(r["t_step_ms"] * 1e3, 2)
+    if uniq != logical:
+        e["kv_gbs_logical"] = round(logical / t_dec / 1e9, 1)
+    if fl:
+        tf = float(np.median(fl)) * 1e-3
+        e["flushed"] = {"t_decode_us_median": round(tf * 1e6, 2),
+                        "t_decode_us_p10_p90": [round(float(np.percentile(fl, 10)) * 1e3, 2),
+                                                round(float(np.percentile(fl, 90)) * 1e3, 2)],
+                        "frac": round(uniq / tf / 1e9 / HBM_PEAK_GBS, 4)}
+    if cfg != 0:
+        e["meets_target"] = bool(e["frac"] >= TARGET_FRAC)
+    e.update(_traffic_fields(("fp8_" if fp8 else "")
+                             + (f"cascade_config3_B16_P0" if call == "cascade"
+                                else f"config{cfg}_B{w.block_size}_P{w.partition_size}")))
+    return e
+
+
 def main():
     a = _args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -564,7 +799,6 @@ def main():
         sys.exit(2)
     if a.probe == "read":  # a child process of its own; nothing here touches the GPU
         sys.exit(probe_read())
-    import numpy as np
     import torch
     import paged_kv_cache_155_amd as pa
     from paged_kv_cache_155_amd.workloads import DESCRIPTIONS, make_workload
@@ -588,151 +822,78 @@ def main():
         bench_blocks(a.op, a.pairs, a.steps, None if a.no_cpu_baseline else a)
         return
 
-    w = make_workload(a.config, block_size=a.block_size, partition_size=a.partition_size,
-                      poison=False)
-    P = w.partition_size
-    dev = "cuda"
-
-    def up(x):
-        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-
     fp8 = a.kv_dtype == "fp8"
-    if fp8:
-        from paged_kv_cache_155_amd.workloads import fp8_pools
-        f8 = fp8_pools(w)
-        kc, vc = up(f8.k_cache), up(f8.v_cache)
-        ks, vs = float(f8.k_scale), float(f8.v_scale)
+    K, W = a.steps, a.warmup
+    flush_iters = 0 if a.no_flush else max(K, 10)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush_iters else None
+    if a.config is None:  # the suite: config 2 (B 16) headline + every config
+        suite = SUITE
     else:
-        kc, vc = up(w.k_cache), up(w.v_cache)
-    q = up(w.q)
-    bt, cl = up(w.block_tables), up(w.context_lens)
-    key, val, slots = up(w.key), up(w.value), up(w.slot_mapping)
-    out = torch.empty_like(q)
-    need = pa.decode_workspace_size(w.num_seqs, w.num_heads, w.head_dim, w.block_size,
-                                    w.max_blocks_per_seq, P)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    scale = float(w.scale)
-
-    def write():
-        if fp8:
-            pa.reshape_and_cache_fp8(key, val, kc, vc, slots, ks, vs)
+        bs = a.block_size
+        suite = [(f"config{a.config}_B{bs or 'd'}", a.config, bs, "decode")]
+    entries, head = [], None
+    for label, cfg, bs, call in suite:
+        w = make_workload(cfg, block_size=bs, poison=False,
+                          partition_size=a.partition_size if a.config is not None else None)
+        print(f"[bench] {label}: S={w.num_seqs} H={w.num_heads} D={w.head_dim} "
+              f"B={w.block_size} P={w.partition_size} call={call}", file=sys.stderr, flush=True)
+        if call == "cascade":
+            write, attend, fused, f8 = _cascade_calls(w, fp8)
+            r = measure(write, attend, K, W, flush_iters, scratch, fused=fused)
         else:
-            pa.reshape_and_cache(key, val, kc, vc, slots)
-
-    def attend():
-        if fp8:
-            pa.decode_fp8(out, q, kc, vc, bt, cl, scale, ks, vs, partition_size=P, workspace=ws)
+            write, attend, f8 = _decode_calls(w, fp8, w.partition_size)
+            r = measure(write, attend, K, W, flush_iters, scratch)
+        e = _entry(label, cfg, w, call, fp8, r)
+        entries.append(e)
+        if head is None:
+            head = (w, f8, r, e, cfg)
         else:
-            pa.decode(out, q, kc, vc, bt, cl, scale, partition_size=P, workspace=ws)
+            del w
+        del write, attend, f8
+        torch.cuda.empty_cache()
 
-    def step():
-        write()
-        attend()
-
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if a.flush else None
-
-    K = a.steps
-    stream = torch.cuda.current_stream()
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall = None
-    if scratch is None:
-        # the timed region: K steps back to back, nothing else on the stream
-        # (a timing event between kernels costs a few microseconds itself)
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        t_begin.record(stream)
-        for _ in range(K):
-            step()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-    # the roofline's decode duration: K decode calls back to back between two
-    # HIP events on the stream the library launches on (mean per call)
-    t_dec_b2b = None
-    if scratch is None:
-        d0 = torch.cuda.Event(enable_timing=True)
-        d1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        d0.record(stream)
-        for _ in range(K):
-            attend()
-        d1.record(stream)
-        torch.cuda.synchronize()
-        t_dec_b2b = d0.elapsed_time(d1) / K
-    # per call: K more steps with HIP events around each call (their spread,
-    # and the reshape_and_cache time; an event pair costs a few microseconds)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    wall1 = time.perf_counter()
-    for i in range(K):
-        if scratch is not None:
-            scratch.fill_(i & 0xFF)  # evict the L2s and the 256 MB MALL
-        ev[i][0].record(stream)
-        write()
-        ev[i][1].record(stream)
-        attend()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    if wall is None:
-        wall = time.perf_counter() - wall1
-    rc_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    t_dec_events = float(np.mean(dec_ms))
-    t_dec = t_dec_b2b if t_dec_b2b is not None else t_dec_events
-    t_rc = float(np.mean(rc_ms))
-    if scratch is None:
-        ms_step = t_begin.elapsed_time(t_end) / K
-    else:  # the flushes are not part of a step
-        ms_step = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
-    kvb = w.kv_bytes() // 2 if fp8 else w.kv_bytes()
-    # the HBM roofline counts each physical block once (a block that several
-    # tables share is read from HBM once; its other reads hit the caches)
-    uniq = w.unique_kv_bytes() // (2 if fp8 else 1)
+    w, f8, r, e, cfg = head
+    ms_step = r["t_step_ms"]
+    t_dec = r["t_decode_ms"]
+    kvb = e["kv_bytes_logical"]
+    uniq = e["kv_bytes_unique"]
     achieved = uniq / (t_dec * 1e-3) / 1e9
     value = kvb / (ms_step * 1e-3) / 1e9
-
+    mp = _measured_peak()
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
-        "warmup": a.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
+        "warmup": W, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3" if fp8 else "f16",
         "data": "synthetic",
         "config": {
-            "workload": f"config{a.config}: {DESCRIPTIONS[a.config]}",
+            "workload": f"config{cfg}: {DESCRIPTIONS[cfg]}",
             "num_seqs": w.num_seqs, "num_heads": w.num_heads, "head_dim": w.head_dim,
-            "block_size": w.block_size, "partition_size": P, "num_blocks": w.num_blocks,
-            "kv_dtype": a.kv_dtype, "kv_bytes_per_step": kvb,
+            "block_size": w.block_size, "partition_size": w.partition_size,
+            "num_blocks": w.num_blocks, "kv_dtype": a.kv_dtype, "kv_bytes_per_step": kvb,
             "unique_kv_bytes": uniq,
             "decode_tokens_per_s_per_layer": round(w.num_seqs / (ms_step * 1e-3), 1),
             "decode_only_tokens_per_s_per_layer": round(w.num_seqs / (t_dec * 1e-3), 1),
             "t_decode_us_mean": round(t_dec * 1e3, 2),
-            "t_decode_us_events_mean": round(t_dec_events * 1e3, 2),
-            "t_decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
-            "t_decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
-                                    round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
-            "t_reshape_us_mean": round(t_rc * 1e3, 2),
-            "t_step_instrumented_us_mean": round(float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
-                                                 * 1e3, 2),
-            "wall_s_timed": round(wall, 4), "accumulate": "f32", "flush": bool(a.flush),
+            "t_reshape_us_mean": round(r["t_reshape_ms"] * 1e3, 2),
+            "wall_s_timed": round(r["wall_s"], 4), "accumulate": "f32",
+            "timing": "value and ms_per_step: K steps (reshape_and_cache + decode) back to back "
+                      "between two HIP events; roofline: K decode calls back to back",
             "device": _device_info(torch),
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "bytes": "unique K/V bytes" + (" (logical: %.1f GB/s)" % (kvb / (t_dec * 1e-3) / 1e9)
-                                                    if uniq != kvb else ""),
-                     "measured_peak": _measured_peak(),
-                     "frac_of_measured": (round(achieved / _measured_peak(), 4)
-                                          if _measured_peak() else None),
-                     "traffic": _traffic(("fp8_" if fp8 else "") + f"config{a.config}_B{w.block_size}_P{P}"),
+                     "bytes": "unique K/V bytes",
+                     "measured_peak": mp,
+                     "frac_of_measured": round(achieved / mp, 4) if mp else None,
+                     "traffic": e["traffic"], "traffic_source": e["traffic_source"],
                      "kernel": ("pa_decode_fp8" if fp8 else "pa_decode")
-                               + " (partition kernel + reduce kernel): HIP events around "
-                               + ("K calls back to back" if t_dec_b2b is not None
-                                  else "each call after a 1 GiB flush")},
+                               + " (partition kernel + reduce kernel): HIP events around K "
+                                 "calls back to back"},
+        "per_config": entries,
         "cpu_baseline": None,
     }
+    if "flushed" in e:
+        line["roofline"]["flushed"] = e["flushed"]
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens, a.cpu_repeats, a.cpu_seconds,
                                             f8 if fp8 else None)
