@@ -55,7 +55,8 @@ enum {
     PA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than pa_decode_workspace_size */
     PA_ERR_ALIGN = -6,       /* a base pointer is not 16-byte aligned                */
     PA_ERR_HIP = -7,         /* the HIP runtime reported an error at launch          */
-    PA_ERR_RANGE = -8        /* a host-side block index is outside its cache          */
+    PA_ERR_RANGE = -8,       /* a host-side block index is outside its cache          */
+    PA_ERR_SCRATCH = -9      /* pa_decode_noalloc: partials exceed its static scratch  */
 };
 
 /*
@@ -144,6 +145,36 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
               int32_t max_blocks_per_seq, float scale, int32_t partition_size,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, semantics, result bits and errors as pa_decode, without
+ * the workspace arguments.  The split-context partials go to a static device
+ * array of PA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on (from the first call on that GPU until the process ends); the
+ * call itself allocates and frees nothing.
+ *   - A call whose pa_decode_workspace_size(...) exceeds
+ *     PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_SCRATCH and enqueues nothing
+ *     (32 MiB holds, e.g., 256 sequences x 40 heads x 4 partitions of
+ *     head_dim 128: 21 MB).
+ *   - The scratch is that of the calling thread's current device; `stream`
+ *     must belong to that device.
+ *   - Every call on a GPU shares that GPU's array, and nothing in it has to
+ *     start at zero (each partition writes its slot before the merge reads
+ *     it).  Calls that may overlap in time on one GPU (on different streams
+ *     without an ordering between them) race on the array; calls on one
+ *     stream are ordered and safe.
+ * The first call on a device looks the array's address up
+ * (hipGetSymbolAddress); a failure there returns PA_ERR_HIP.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                      int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+                      void* stream);
 
 /*
  * Decode for a batch whose sequences all begin with the same shared prefix

@@ -6,10 +6,10 @@ input generator (workloads).
 """
 from ._binding import (PAError, copy_blocks, decode, decode_cascade, decode_cascade_append,
                        decode_cascade_append_fp8, decode_cascade_fp8, decode_cascade_workspace_size, decode_fp8,
-                       decode_workspace_size, load, multi_query, multi_query_fp8,
+                       decode_noalloc, decode_workspace_size, load, multi_query, multi_query_fp8,
                        reshape_and_cache, reshape_and_cache_fp8, status_string, swap_blocks)
 
 __all__ = ["PAError", "copy_blocks", "decode", "decode_cascade", "decode_cascade_append",
            "decode_cascade_append_fp8", "decode_cascade_fp8", "decode_cascade_workspace_size", "decode_fp8",
-           "decode_workspace_size", "load", "multi_query", "multi_query_fp8", "reshape_and_cache",
+           "decode_noalloc", "decode_workspace_size", "load", "multi_query", "multi_query_fp8", "reshape_and_cache",
            "reshape_and_cache_fp8", "status_string", "swap_blocks"]

@@ -50,6 +50,8 @@ def load(path=None):
     lib.pa_decode.argtypes = ([_P] * 6 + [_I32] * 6 + [ctypes.c_float, _I32, _P, ctypes.c_size_t,
                                                        _P])
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [_P] * 6 + [_I32] * 6 + [ctypes.c_float, _I32, _P]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_reshape_and_cache_fp8.argtypes = ([_P, _P, _P, _P, _P] + [_I32] * 5
                                              + [ctypes.c_float, ctypes.c_float, _P])
     lib.pa_reshape_and_cache_fp8.restype = ctypes.c_int
@@ -185,6 +187,33 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, partitio
                           _ptr(workspace), wbytes, _stream_ptr(stream))
     if rc != PA_OK:
         raise PAError(rc, "pa_decode")
+    return out
+
+
+def decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                   partition_size=512, stream=None):
+    """decode() that allocates nothing: the split partials go to the library's
+    static per-GPU scratch (PA_NOALLOC_SCRATCH_BYTES, 32 MiB).  Calls that
+    may overlap in time on one GPU (different streams, unordered) race on
+    that scratch.  A split whose partials do not fit raises PAError
+    (PA_ERR_SCRATCH)."""
+    import torch
+    _check(k_cache, "k_cache", torch.float16, ndim=4)
+    NB, B, H, D = k_cache.shape
+    _check(v_cache, "v_cache", torch.float16, shape=k_cache.shape)
+    _check(q, "q", torch.float16, ndim=3)
+    S = q.shape[0]
+    _check(q, "q", torch.float16, shape=(S, H, D))
+    _check(out, "out", torch.float16, shape=(S, H, D))
+    _check(block_tables, "block_tables", torch.int32, ndim=2)
+    MB = block_tables.shape[1]
+    _check(block_tables, "block_tables", torch.int32, shape=(S, MB))
+    _check(context_lens, "context_lens", torch.int32, shape=(S,))
+    rc = load().pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(block_tables), _ptr(context_lens), S, H, D, NB, B, MB,
+                                  float(scale), int(partition_size), _stream_ptr(stream))
+    if rc != PA_OK:
+        raise PAError(rc, "pa_decode_noalloc")
     return out
 
 

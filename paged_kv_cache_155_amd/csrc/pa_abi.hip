@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -64,6 +65,9 @@ const char* pa_status_string(int status)
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a base pointer is not 16-byte aligned";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported a launch error";
     case PA_ERR_RANGE: return "PA_ERR_RANGE: a block index is outside its cache";
+    case PA_ERR_SCRATCH:
+        return "PA_ERR_SCRATCH: the split-context partials need more than the "
+               "PA_NOALLOC_SCRATCH_BYTES (32 MiB) of pa_decode_noalloc's static scratch";
     default: return "unknown pa status";
     }
 }
@@ -490,6 +494,75 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                             partition_size, workspace, workspace_bytes);
     if (rc != PA_OK)
         return rc == 1 ? PA_OK : rc;
+    hipError_t e = pa::launch_decode_dispatch(p, head_dim, block_size,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// ---- pa_decode_noalloc: the split partials in a static device array ----
+namespace {
+
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "whole 256-byte pieces");
+
+// The partials of pa_decode_noalloc.  Each GPU holds its own copy of this
+// array (from the first call on it until the process ends), at its own
+// address: host code uses the address hipGetSymbolAddress returns with that
+// device current, never the array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device id
+
+// Address of the current device's scratch, looked up once per device.
+int current_scratch(void** ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return PA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return PA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                      int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+                      void* stream)
+{
+    // Every host check first, with no workspace: only the workspace check can
+    // then fail, and only when the call splits.
+    pa::DecodeParams p;
+    int rc = prepare_decode(p, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                            num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
+                            scale, partition_size, nullptr, 0);
+    if (rc == 1)
+        return PA_OK;  // nothing to enqueue
+    if (rc == PA_ERR_WORKSPACE) {
+        const size_t need = pa_decode_workspace_size(num_seqs, num_heads, head_dim, block_size,
+                                                     max_blocks_per_seq, partition_size);
+        if (need > kScratchBytes)
+            return PA_ERR_SCRATCH;
+        void* ws = nullptr;
+        rc = current_scratch(&ws);
+        if (rc != PA_OK)
+            return rc;
+        rc = prepare_decode(p, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                            num_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
+                            scale, partition_size, ws, kScratchBytes);
+    }
+    if (rc != PA_OK)
+        return rc;
     hipError_t e = pa::launch_decode_dispatch(p, head_dim, block_size,
                                               static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
