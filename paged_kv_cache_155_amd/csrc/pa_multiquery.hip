@@ -35,8 +35,7 @@
 //                        sum stays per lane until the end; the reference max
 //                        moves, and O is rescaled, only when some row's chunk
 //                        max passes it by more than 2^8 (lazy rescaling); the
-//                        weights are rounded to fp16 for the product below and
-//                        the sum adds the rounded weights
+//                        sum adds fp32 weights, P.V their fp16 roundings
 //       O^T += V^T P^T   v_mfma_f32_16x16x32_f16 over 32 tokens; the S^T
 //                        tiles are already P^T in the B-operand layout, and
 //                        the V^T operand comes from the transposing LDS read
@@ -409,17 +408,18 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
                 alpha[qt] = up ? exp2_fast(m[qt] - m_ref) : 1.0f;
                 moved |= up;
                 m[qt] = m_new;
-                // The weights enter P.V rounded to fp16, and the row sum adds
-                // those same rounded weights, so numerator and denominator agree.
+                // The row sum adds the fp32 weights; P.V takes the same weights
+                // rounded to fp16 (the B operand), so numerator and denominator
+                // differ by at most 2^-11 relative per weight.  Summing the
+                // rounded weights instead measured 1.5% slower.
                 float psum = 0.0f;
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const _Float16 p = (_Float16)exp2_fast(
-                            __builtin_fmaf(st[qt][s][j], P.scale_log2, -m_ref));
-                        psum += (float)p;
-                        pb[qt][s / 2][4 * (s % 2) + j] = p;
+                        const float p = exp2_fast(__builtin_fmaf(st[qt][s][j], P.scale_log2, -m_ref));
+                        psum += p;
+                        pb[qt][s / 2][4 * (s % 2) + j] = (_Float16)p;
                     }
                 lpart[qt] = lpart[qt] * alpha[qt] + psum;
             }
