@@ -79,6 +79,12 @@ def _args():
                          "3); multi_query: a chunked-prefill batch through pa_multi_query")
     ap.add_argument("--pairs", type=int, default=1024, help="blocks per copy/swap call")
     ap.add_argument("--probe", choices=["copy", "read"], default=None)
+    ap.add_argument("--call", choices=["decode", "cascade"], default="decode",
+                    help="with --config: the entry point timed (cascade: config 3 through "
+                         "pa_decode_cascade, its 32 shared blocks as the prefix table)")
+    ap.add_argument("--ingest-traffic", nargs=3, metavar=("KEY", "FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the FETCH_SIZE / WRITE_SIZE counter csvs of rocprofv3 "
+                         "--pmc runs of one workload into profiles/traffic.json[KEY]")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the flushed decode timings (a 1 GiB write before each call "
                          "evicts the L2s and the MALL)")
@@ -789,8 +795,65 @@ def _entry(label, cfg, w, call, fp8, r):
     return e
 
 
+def _workload_bytes(key):
+    """(algorithmic K/V bytes, unique K/V bytes) of the workload a traffic key
+    names (config{c}_B{b}_P{p}, cascade_config3_B16_P0,
+    multi_query_16x2048_last512; fp8_ prefix: one byte per element)."""
+    from paged_kv_cache_155_amd.workloads import make_workload
+    fp8 = key.startswith("fp8_")
+    k = key[4:] if fp8 else key
+    eb = 1 if fp8 else 2
+    if k.startswith("multi_query_16x2048"):
+        n = 16 * 2048 * 32 * 128 * 2 * eb
+        return n, n
+    if k.startswith("cascade_config3"):
+        w = make_workload(3, poison=False)
+    else:
+        cfg = int(k[len("config"):].split("_")[0])
+        bsz = int(k.split("_B")[1].split("_")[0])
+        w = make_workload(cfg, block_size=bsz, poison=False)
+    return w.kv_bytes() * eb // 2, w.unique_kv_bytes() * eb // 2
+
+
+def ingest_traffic(key, fetch_csv, write_csv):
+    """profiles/traffic.json[key] from rocprofv3 --pmc FETCH_SIZE and
+    WRITE_SIZE csvs of one workload: the median per dispatch of each library
+    kernel (the step's reshape_and_cache excluded), summed over the kernels
+    of one call and scaled to bytes by the calibration entry."""
+    import csv
+    import statistics
+    from collections import defaultdict
+    tj = json.load(open(TRAFFIC_JSON))
+    cal = tj["_calibration"]
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            if r["Counter_Name"] != counter or "pa::" not in name or "reshape_and_cache" in name:
+                continue
+            name = name.replace("void ", "").replace("pa::(anonymous namespace)::", "")
+            vals[name.split("(pa::")[0]].append(float(r["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in vals.items()}
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    rd = sum(f.values()) * 1024 * cal["fetch_scale"]
+    wr = sum(w.values()) * 1024 * cal["write_scale"]
+    alg, uniq = _workload_bytes(key)
+    tj[key] = {"kernel_code_sha": kernel_code_sha(), "bytes_per_launch": int(round(rd + wr)),
+               "read_bytes": int(round(rd)), "write_bytes": int(round(wr)),
+               "read_over_unique": round(rd / uniq, 4),
+               "fetch_size_kib": f, "write_size_kib": w,
+               "algorithmic_kv_bytes": alg, "unique_kv_bytes": uniq}
+    json.dump(tj, open(TRAFFIC_JSON, "w"), indent=1)
+    print(json.dumps({key: tj[key]}))
+
+
 def main():
     a = _args()
+    if a.ingest_traffic:
+        ingest_traffic(*a.ingest_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}): "
@@ -830,7 +893,8 @@ def main():
         suite = SUITE
     else:
         bs = a.block_size
-        suite = [(f"config{a.config}_B{bs or 'd'}", a.config, bs, "decode")]
+        suite = [(f"config{a.config}_B{bs or 'd'}" + ("_cascade" if a.call == "cascade" else ""),
+                  a.config, bs, a.call)]
     entries, head = [], None
     for label, cfg, bs, call in suite:
         w = make_workload(cfg, block_size=bs, poison=False,
@@ -839,7 +903,8 @@ def main():
               f"B={w.block_size} P={w.partition_size} call={call}", file=sys.stderr, flush=True)
         if call == "cascade":
             write, attend, fused, f8 = _cascade_calls(w, fp8)
-            r = measure(write, attend, K, W, flush_iters, scratch, fused=fused)
+            r = measure(write, attend, K, W, flush_iters, scratch,
+                        fused=fused if a.config is None else None)
         else:
             write, attend, f8 = _decode_calls(w, fp8, w.partition_size)
             r = measure(write, attend, K, W, flush_iters, scratch)
@@ -886,9 +951,10 @@ def main():
                      "measured_peak": mp,
                      "frac_of_measured": round(achieved / mp, 4) if mp else None,
                      "traffic": e["traffic"], "traffic_source": e["traffic_source"],
-                     "kernel": ("pa_decode_fp8" if fp8 else "pa_decode")
-                               + " (partition kernel + reduce kernel): HIP events around K "
-                                 "calls back to back"},
+                     "kernel": e["call"] + (" (shared-prefix pass + partition kernel)"
+                                            if "cascade" in e["call"]
+                                            else " (partition kernel + reduce kernel)")
+                               + ": HIP events around K calls back to back"},
         "per_config": entries,
         "cpu_baseline": None,
     }
