@@ -118,7 +118,8 @@ def kernel_code_sha():
     from paged_kv_cache_155_amd import _build
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
                   + [os.path.join(ROOT, "include", "pa.h")])
-    return hashlib.sha256((_code_sha(*srcs) + " ".join(_build.FLAGS)).encode()).hexdigest()[:16]
+    flags = " ".join(f for f in _build.FLAGS if not f.startswith("-I"))  # no checkout paths
+    return hashlib.sha256((_code_sha(*srcs) + flags).encode()).hexdigest()[:16]
 
 
 def _traffic(config_name):
