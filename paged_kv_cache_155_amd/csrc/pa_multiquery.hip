@@ -30,12 +30,13 @@
 //                        group owns a contiguous quarter of the dims, so K and
 //                        Q are read as they lie)
 //       online softmax   per query column (lane = query, 16 tokens per lane),
-//                        base-2 exponent; the running max is exchanged across
-//                        the four lane groups with permlane swaps, the running
-//                        sum stays per lane until the end; the reference max
-//                        moves, and O is rescaled, only when some row's chunk
-//                        max passes it by more than 2^8 (lazy rescaling); the
-//                        sum adds fp32 weights, P.V their fp16 roundings
+//                        base-2 exponent against a lazy reference: the scores
+//                        are shifted by it, and only when a shifted score in the
+//                        wave passes 2^8 (or a reference is unset) are the row
+//                        maxima exchanged across the four lane groups (permlane
+//                        swaps), the reference moved and O rescaled
+//       l += ones P^T    the row sums on the matrix cores: the fp16 weights
+//                        that P.V takes, summed in fp32
 //       O^T += V^T P^T   v_mfma_f32_16x16x32_f16 over 32 tokens; the S^T
 //                        tiles are already P^T in the B-operand layout, and
 //                        the V^T operand comes from the transposing LDS read
@@ -96,20 +97,13 @@ __device__ __forceinline__ s4 ds_read_tr16(const _Float16* p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
 }
 
-// max / sum over the four 16-lane groups (lanes c, c+16, c+32, c+48)
+// max over the four 16-lane groups (lanes c, c+16, c+32, c+48)
 __device__ __forceinline__ float group_max(float x)
 {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group_sum(float x)
-{
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 }  // namespace
@@ -266,16 +260,20 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
             qf[qt][i] = r < n_rows ? qp[i] : u32x4{0, 0, 0, 0};
     }
 
-    f4 o[QT][NB];
-    float m[QT], lpart[QT];  // running max (scaled, base 2) and this lane's share of the sum
+    // O^T, the row sums (every element of lsum[qt] holds the sum of query c), and
+    // the reference the exponentials are taken against (scaled, base 2)
+    f4 o[QT][NB], lsum[QT];
+    float m[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         m[qt] = kNegInf;
-        lpart[qt] = 0.0f;
+        lsum[qt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             o[qt][nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    // all-ones A operand: ones * P^T sums the fp16 weights that P.V takes
+    const h8 ones = h8{1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
 
     // ---- loader role: 4 tokens (4*lq .. 4*lq+3 of the chunk) x dims 8*lp .. 8*lp+7 ----
     const bool loader = UNITS == kMqThreads || tid < UNITS;  // a constant when all threads load
@@ -350,9 +348,9 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
 
         if (wrows > 0 && t0 < wave_hi) {  // wave-uniform: some row of this wave sees the chunk
             // S^T[token 16s + 4g + j][query c] for the four 16-token subtiles
-            f4 st[QT][4];
+            f4 st[QT][N / 16];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < N / 16; ++s) {
                 u32x4 ka[KI];
 #pragma unroll
                 for (int i = 0; i < KI; ++i)
@@ -375,7 +373,7 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
                 for (int qt = 0; qt < QT; ++qt) {
                     const int nvis = lim[qt] - t0 - 4 * g;  // visible offsets 16s + j < nvis
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
+                    for (int s = 0; s < N / 16; ++s)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             if (16 * s + j >= nvis)
@@ -383,53 +381,84 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
                 }
             }
 
-            // online softmax per query column; P^T as the B operand of the next product
-            h8 pb[QT][2];
-            bool moved = false;
-            float alpha[QT];
+            // Online softmax per query column, against a lazy reference m (scaled,
+            // base 2): the exponentials are taken against m, which moves (and O and
+            // the row sums are rescaled) only when a chunk's max passes it by more
+            // than kLazyRescale, so every weight stays below 2^kLazyRescale, far
+            // inside fp16; the result is the same softmax, since O and l share the
+            // reference.  The scores are shifted against the current reference
+            // first; only when some shifted score in the wave passes the threshold,
+            // or a reference is not yet set, are the row maxima formed and the
+            // reference moved (the shift then corrected) -- the same decisions as
+            // forming every chunk's max, at none of its cost in the usual chunk.
+            float m_ref[QT];
+            float tmax = kNegInf;
+            bool unset = false;
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) {
-                float bmax = kNegInf;
+                m_ref[qt] = m[qt] == kNegInf ? 0.0f : m[qt];
+                unset |= m[qt] == kNegInf;
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        bmax = fmaxf(bmax, st[qt][s][j]);
-                // scale > 0, so the max of the raw scores gives the max of the scaled ones.
-                // m is the reference the exponentials are taken against, moved (and O, l
-                // rescaled) only when a chunk's max passes it by more than kLazyRescale:
-                // the weights then stay below 2^kLazyRescale, far inside fp16 and fp32,
-                // and the rescale of O is skipped in most chunks (the result is the same
-                // softmax: O and l share the reference).
-                const float cm = group_max(bmax) * P.scale_log2;
-                const bool up = cm > m[qt] + kLazyRescale;  // any finite cm while m = -inf
-                const float m_new = up ? cm : m[qt];
-                const float m_ref = m_new == kNegInf ? 0.0f : m_new;
-                alpha[qt] = up ? exp2_fast(m[qt] - m_ref) : 1.0f;
-                moved |= up;
-                m[qt] = m_new;
-                // The row sum adds the fp32 weights; P.V takes the same weights
-                // rounded to fp16 (the B operand), so numerator and denominator
-                // differ by at most 2^-11 relative per weight.  Summing the
-                // rounded weights instead measured 1.5% slower.
-                float psum = 0.0f;
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
+                for (int s = 0; s < N / 16; ++s)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float p = exp2_fast(__builtin_fmaf(st[qt][s][j], P.scale_log2, -m_ref));
-                        psum += p;
-                        pb[qt][s / 2][4 * (s % 2) + j] = (_Float16)p;
+                        // scale > 0: the shifted scores keep the order of the raw ones
+                        st[qt][s][j] = __builtin_fmaf(st[qt][s][j], P.scale_log2, -m_ref[qt]);
+                        tmax = fmaxf(tmax, st[qt][s][j]);
                     }
-                lpart[qt] = lpart[qt] * alpha[qt] + psum;
             }
-            if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+            if (__builtin_amdgcn_ballot_w64(unset || tmax > kLazyRescale) != 0) {
+                bool moved = false;
+                float alpha[QT];
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) {
+                    float bmax = kNegInf;
+#pragma unroll
+                    for (int s = 0; s < N / 16; ++s)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            bmax = fmaxf(bmax, st[qt][s][j]);
+                    const float cm = group_max(bmax) + m_ref[qt];  // -inf stays -inf
+                    const bool up = cm > m[qt] + kLazyRescale;    // any finite cm while m = -inf
+                    const float m_new = up ? cm : m[qt];
+                    const float ref_new = m_new == kNegInf ? 0.0f : m_new;
+                    alpha[qt] = up ? exp2_fast(m[qt] - ref_new) : 1.0f;
+                    moved |= up;
+                    m[qt] = m_new;
+                    const float shift = ref_new - m_ref[qt];
+#pragma unroll
+                    for (int s = 0; s < N / 16; ++s)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            st[qt][s][j] -= shift;
+                }
+                if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+                    for (int qt = 0; qt < QT; ++qt) {
+                        lsum[qt] *= alpha[qt];
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            o[qt][nb] *= alpha[qt];
+                    }
+                }
+            }
+            // the weights, rounded to fp16 as P^T, the B operand of the next products
+            h8 pb[QT][N / 32];
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                for (int s = 0; s < N / 16; ++s)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pb[qt][s / 2][4 * (s % 2) + j] = (_Float16)exp2_fast(st[qt][s][j]);
+
+            // Row sums: ones * P^T over the chunk's tokens, the fp16 weights that
+            // P.V takes summed in fp32 (numerator and denominator share them).
+#pragma unroll
+            for (int kk = 0; kk < N / 32; ++kk)
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        o[qt][nb] *= alpha[qt];
-            }
+                    lsum[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[qt][kk], lsum[qt], 0, 0, 0);
 
             // O^T[dim 16nb + 4g + j][query c] += V^T P^T over the chunk's 64 tokens.
             // B element 4*(s%2)+j of step kk is token 32kk + 16(s%2) + 4g + j; the
@@ -442,7 +471,7 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
+                for (int kk = 0; kk < N / 32; ++kk) {
                     const s4 lo = ds_read_tr16(&vsrc[(32 * kk) * VS + 16 * nb]);
                     const s4 hi = ds_read_tr16(&vsrc[(32 * kk + 16) * VS + 16 * nb]);
                     const h8 va = __builtin_bit_cast(
@@ -460,12 +489,12 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     // ---- O^T[dim 16nb + 4g + j][query c] / l(query c) ----
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-        const float lsum = group_sum(lpart[qt]);
+        const float l = lsum[qt][0];
         const int r = wr0 + 16 * qt + c;
         if (r >= n_rows)
             continue;
         // FP8: the V scale (the K scale is in scale_log2)
-        const float inv = (lsum > 0.0f ? 1.0f / lsum : 0.0f) * (kFp8 ? P.v_scale : 1.0f);
+        const float inv = (l > 0.0f ? 1.0f / l : 0.0f) * (kFp8 ? P.v_scale : 1.0f);
         if constexpr (kCascade) {
             const int64_t u = ((row0 + r) * P.num_heads + h) * P.num_slots + part;
 #pragma unroll
@@ -473,7 +502,7 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
                 *reinterpret_cast<f4*>(&P.ws_o[u * D + nb * 16 + 4 * g]) = o[qt][nb] * inv;
             if (g == 0) {
                 P.ws_m[u] = m[qt];
-                P.ws_l[u] = lsum;
+                P.ws_l[u] = l;
             }
         } else {
             _Float16* orow = P.out + ((row0 + r) * P.num_heads + h) * D;
