@@ -20,11 +20,13 @@
 //     decode reduce merges with the partials of the private suffixes.
 //
 // Per 64-token chunk of the stream:
-//   * the 256 threads load it once (each: 4 consecutive tokens x 8 dims of
-//     K and of V, 16-byte loads through the block table) and stage it in LDS
-//     in its row layout (rows padded to D+8 halves for K, D+16 for V), double
-//     buffered so one barrier per chunk suffices; the next chunk's loads are
-//     issued before the math;
+//   * the workgroup loads it once into LDS, [token][dim] tiles with unpadded
+//     rows whose 16-byte pieces are XOR-swizzled by row (so the operand reads
+//     below fall on distinct banks), double buffered so one barrier per chunk
+//     suffices; the next chunk is loaded while this one is computed.  fp16
+//     caches go straight to LDS (buffer loads with an LDS destination, 1 KiB
+//     per wave instruction, one block per wave and chunk); FP8 caches pass
+//     through registers, where they are widened to fp16;
 //   * each wave, for its 16 * QT rows:
 //       S^T = K Q^T      v_mfma_f32_16x16x32_f16 over the head dim (each lane
 //                        group owns a contiguous quarter of the dims, so K and
@@ -40,9 +42,7 @@
 //       O^T += V^T P^T   v_mfma_f32_16x16x32_f16 over 32 tokens; the S^T
 //                        tiles are already P^T in the B-operand layout, and
 //                        the V^T operand comes from the transposing LDS read
-//                        ds_read_b64_tr_b16 on the row-layout V tile (the
-//                        D+16 stride keeps its 16-lane groups on distinct
-//                        banks)
+//                        ds_read_b64_tr_b16 on the [token][dim] V tile
 // Positions past a row's limit get -inf scores; K/V rows past the stream end
 // are loaded as zeros (select, not multiply), so unread slots may hold
 // anything.
@@ -60,6 +60,11 @@ constexpr int kWaves = kMqThreads / kWave;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyRescale = 8.0f;  // log2 units: weights stay below 256
 constexpr int kCopyItems = 4;         // new-row pieces per thread of a copy workgroup
+// s_waitcnt vmcnt(0), the other counters left alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+// the last word of a raw buffer resource on gfx9 parts (32-bit data, no swizzle)
+constexpr int kBufferFlags = 0x00020000;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -131,6 +136,27 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n)
     return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
 
+// LDS tiles are [token][dim] with unpadded rows; the 16-byte piece p (dims
+// 8p .. 8p+7) of row r is stored at piece p ^ swz(r).  With 64 banks of 4
+// bytes, a 256-byte span holds 256 / (2 D) rows.  K (read 16 bytes per lane,
+// the 16 lanes of a group on 16 consecutive rows): the rows sharing a span
+// half get distinct pieces.  V (read with the transposing 8-byte read, the 16
+// lanes of a group on 4 consecutive rows x 2 pieces x 2 halves): the shift by
+// one bit keeps the piece's low bit free for the two pieces of a row.
+// 16 bytes per lane from base + voff into LDS at lds + 16 * lane: a buffer
+// load through a resource on base (scalar registers), so the lane offset is
+// the only vector operand
+__device__ __forceinline__ void load_lds16(const char* base, _Float16* lds, uint32_t voff)
+{
+    typedef __attribute__((address_space(3))) void lds_void;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7fffffff, kBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int D> __device__ __forceinline__ int swz_k(int r) { return (r / (128 / D)) % (D / 8); }
+template <int D> __device__ __forceinline__ int swz_v(int r) { return (2 * (r / (128 / D))) % (D / 8); }
+
 // Appending form of the shared-prefix pass: the first workgroups of the grid
 // copy this step's new K/V rows (row s of new_k / new_v [S, H, D]) to their
 // slots, 16 bytes of K and of V per item, kCopyItems items per thread with
@@ -181,18 +207,18 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     constexpr int N = kMqChunk;           // tokens per staged chunk
     constexpr int NB = D / 16;            // 16-dim blocks of O^T
     constexpr int KI = D / 32;            // MFMA k-steps over the head dim
-    constexpr int KS = D + 8;             // LDS row stride (halves) of the K tile
-    constexpr int VS = D + 16;            // LDS row stride (halves) of the V tile
     constexpr int WROWS = 16 * QT;        // query rows per wave
     constexpr int ROWS = kWaves * WROWS;  // query rows per workgroup
     constexpr int DG = D / 8;             // 8-dim groups per token row
     constexpr int UNITS = (N / 4) * DG;   // 4-token x 8-dim load units per chunk
+    constexpr int RPI = 64 / DG;          // rows per direct-to-LDS load (64 lanes x 16 bytes)
+    constexpr int DJ = 16 / RPI;          // direct loads per wave and tile (its 16 rows)
     static_assert(N == 64 && UNITS <= kMqThreads && DG <= 16, "chunk geometry");
-    static_assert(B % 4 == 0, "a 4-token load unit must stay inside one physical block");
+    static_assert(B % 16 == 0, "a wave's 16 rows of a chunk must stay inside one physical block");
     static_assert(ROWS == (kCascade ? kCascadeTileRows : kMqTileRows), "tile rows");
 
-    __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][N * KS];  // [token][dim]
-    __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][N * VS];  // [token][dim]
+    __shared__ __attribute__((aligned(16))) _Float16 k_lds[2][N * D];  // [token][dim], swizzled
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][N * D];
 
     uint32_t wg = blockIdx.x;
     if constexpr (kCascade) {
@@ -275,16 +301,68 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
     // all-ones A operand: ones * P^T sums the fp16 weights that P.V takes
     const h8 ones = h8{1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
 
-    // ---- loader role: 4 tokens (4*lq .. 4*lq+3 of the chunk) x dims 8*lp .. 8*lp+7 ----
-    const bool loader = UNITS == kMqThreads || tid < UNITS;  // a constant when all threads load
-    const int lp = tid % DG, lq = tid / DG;
     const int64_t block_elems = (int64_t)B * P.num_heads * D;
     const int token_stride = P.num_heads * D;
-    typedef typename Raw8<kFp8>::type Raw;
     constexpr int EB = kFp8 ? 1 : 2;  // bytes per cache element
     const char* k_bytes = static_cast<const char*>(P.k_cache);
     const char* v_bytes = static_cast<const char*>(P.v_cache);
-    Raw kr[4], vr[4];
+
+    // ---- fp16 caches: direct-to-LDS loads.  Wave w fills rows 16w .. 16w+15 of
+    // both tiles, RPI rows (1 KiB) per load: lane l of load j takes row
+    // r = 16w + RPI j + l / DG and stored piece l % DG, i.e. source piece
+    // (l % DG) ^ swz(r).  A chunk starts at a multiple of 64 tokens, so the 16
+    // rows of a wave lie in one physical block, whose id is read once per wave
+    // (a scalar read, one chunk ahead) and whose lane offsets do not change.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t dk[DJ], dv[DJ];  // byte offsets of this lane's sources inside a block
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) {
+        const int r = 16 * wave + RPI * j + lane / DG;
+        const uint32_t row = (uint32_t)((r % B) * token_stride + h * D) * 2u;
+        dk[j] = row + (uint32_t)(((lane % DG) ^ swz_k<D>(r)) * 16);
+        dv[j] = row + (uint32_t)(((lane % DG) ^ swz_v<D>(r)) * 16);
+    }
+    // the block of this wave's rows of the chunk at t0 (clamped into the stream;
+    // a wave whose rows all lie past the stream end loads nothing).  A vector
+    // read (the direct loads count as clobbers of global memory, so the compiler
+    // will not make it a scalar one), issued before a chunk's direct loads and
+    // made uniform only after the wait that lands them: taken earlier, it would
+    // wait for every load issued before it.
+    auto wave_block = [&](int t0) { return table[min(t0 + 16 * wave_u, stream_end - 1) / B]; };
+    auto dma_chunk = [&](int t0, int b, int blk) {
+        if (t0 + 16 * wave_u >= stream_end)
+            return;
+        const char* kb = k_bytes + (int64_t)blk * block_elems * 2;
+        const char* vb = v_bytes + (int64_t)blk * block_elems * 2;
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+            load_lds16(kb, &k_lds[b][(16 * wave_u + RPI * j) * D], dk[j]);
+            load_lds16(vb, &v_lds[b][(16 * wave_u + RPI * j) * D], dv[j]);
+        }
+    };
+    // Rows past the stream end (in the last chunk) are zeroed once the direct
+    // loads have landed: unread slots may hold anything, and P.V must not see
+    // it (those positions are masked, but 0 * NaN is NaN).
+    auto zero_tail = [&](int t0, int b) {
+        if (t0 + 16 * wave_u + 16 <= stream_end)
+            return;  // wave-uniform
+#pragma unroll
+        for (int k = 0; k < 16 * DG / kWave; ++k) {
+            const int piece = k * kWave + lane;  // of the wave's 16 rows
+            const int r = 16 * wave_u + piece / DG;
+            if (t0 + r >= stream_end) {
+                *reinterpret_cast<u32x4*>(&k_lds[b][r * D + (piece % DG) * 8]) = u32x4{0, 0, 0, 0};
+                *reinterpret_cast<u32x4*>(&v_lds[b][r * D + (piece % DG) * 8]) = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+
+    // ---- FP8 caches: each thread loads 4 tokens (4*lq .. 4*lq+3 of the chunk) x
+    // 8 dims (8*lp ..) into registers and widens them to fp16 as it stores them
+    const bool loader = UNITS == kMqThreads || tid < UNITS;  // a constant when all threads load
+    const int lp = tid % DG, lq = tid / DG;
+    typedef typename Raw8<kFp8>::type Raw;
+    Raw kr[4], vr[4];  // (unused, and removed, for fp16 caches)
     // The physical block of this thread's four tokens of the chunk at t0 (one
     // block, as 4 divides B).  Loaded a chunk ahead of its K/V loads, so that
     // their addresses never wait on a table read.  The position is clamped
@@ -319,9 +397,25 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
             }
         }
     };
+    auto store_chunk = [&](int b) {
+        if (!loader)
+            return;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * lq + j;
+            *reinterpret_cast<u32x4*>(&k_lds[b][r * D + (lp ^ swz_k<D>(r)) * 8]) = widen8(kr[j]);
+            *reinterpret_cast<u32x4*>(&v_lds[b][r * D + (lp ^ swz_v<D>(r)) * 8]) = widen8(vr[j]);
+        }
+    };
 
-    load_chunk(stream_begin, chunk_block(stream_begin));
-    int next_blk = chunk_block(stream_begin + N);
+    int next_blk;
+    if constexpr (kFp8) {
+        load_chunk(stream_begin, chunk_block(stream_begin));
+        next_blk = chunk_block(stream_begin + N);
+    } else {
+        dma_chunk(stream_begin, 0, __builtin_amdgcn_readfirstlane(wave_block(stream_begin)));
+        next_blk = wave_block(stream_begin + N);
+    }
     // Wait for q here, once: inside the loop the compiler cannot prove these
     // loads complete on every path and would otherwise drain every load in
     // flight (the next chunk's prefetch included) before the first product.
@@ -330,21 +424,43 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
 #pragma unroll
         for (int i = 0; i < KI; ++i)
             asm volatile("" ::"v"(qf[qt][i]));
-    int buf = 0;
-    for (int t0 = stream_begin; t0 < stream_end; t0 += N, buf ^= 1) {
-        _Float16* ks = k_lds[buf];
-        _Float16* vs = v_lds[buf];
-        if (loader) {
+
+    // this lane's operand addresses in a tile (elements): K row 16s + c, pieces
+    // g*KI + i; V^T rows 32kk + 16hh + 4g + c/4, dims 16nb + 4(c%4) .. +3 (the
+    // swizzle of those rows does not depend on kk and hh)
+    int koff[KI], voff[NB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                *reinterpret_cast<u32x4*>(&ks[(4 * lq + j) * KS + 8 * lp]) = widen8(kr[j]);
-                *reinterpret_cast<u32x4*>(&vs[(4 * lq + j) * VS + 8 * lp]) = widen8(vr[j]);
-            }
+    for (int i = 0; i < KI; ++i)
+        koff[i] = c * D + ((g * KI + i) ^ swz_k<D>(c)) * 8;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        voff[nb] = (4 * g + c / 4) * D + ((2 * nb + (c % 4) / 2) ^ swz_v<D>(4 * g + c / 4)) * 8 +
+                   4 * (c % 2);
+
+    // One chunk at t0 in LDS buffer b.  Called with a constant b from a loop
+    // unrolled by two, so the buffer's base folds into the LDS instructions'
+    // immediate offsets.
+    auto step = [&](const int t0, const int b) __attribute__((always_inline)) {
+        const _Float16* ks = k_lds[b];
+        const _Float16* vs = v_lds[b];
+        if constexpr (kFp8) {
+            store_chunk(b);
+            if (t0 + N < stream_end)
+                load_chunk(t0 + N, next_blk);  // in flight during this chunk's math
+            next_blk = chunk_block(t0 + 2 * N);  // unconditional, so no copy waits on it
+        } else {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's direct loads of the chunk landed
+            if (t0 + N > stream_end)
+                zero_tail(t0, b);
         }
-        if (t0 + N < stream_end)
-            load_chunk(t0 + N, next_blk);  // in flight during this chunk's math
-        next_blk = chunk_block(t0 + 2 * N);  // unconditional, so no copy waits on it
         __syncthreads();
+        if constexpr (!kFp8) {
+            // the next chunk into the other buffer, which every wave is done with
+            const int blk = __builtin_amdgcn_readfirstlane(next_blk);
+            next_blk = wave_block(t0 + 2 * N);
+            if (t0 + N < stream_end)
+                dma_chunk(t0 + N, b ^ 1, blk);
+        }
 
         if (wrows > 0 && t0 < wave_hi) {  // wave-uniform: some row of this wave sees the chunk
             // S^T[token 16s + 4g + j][query c] for the four 16-token subtiles
@@ -354,7 +470,7 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
                 u32x4 ka[KI];
 #pragma unroll
                 for (int i = 0; i < KI; ++i)
-                    ka[i] = *reinterpret_cast<const u32x4*>(&ks[(16 * s + c) * KS + g * (D / 4) + 8 * i]);
+                    ka[i] = *reinterpret_cast<const u32x4*>(&ks[16 * s * D + koff[i]]);
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) {
                     f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -392,8 +508,11 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
             // reference moved (the shift then corrected) -- the same decisions as
             // forming every chunk's max, at none of its cost in the usual chunk.
             float m_ref[QT];
-            float tmax = kNegInf;
+            float tmax[N / 16];  // partial maxima, independent chains
             bool unset = false;
+#pragma unroll
+            for (int s = 0; s < N / 16; ++s)
+                tmax[s] = kNegInf;
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) {
                 m_ref[qt] = m[qt] == kNegInf ? 0.0f : m[qt];
@@ -404,10 +523,13 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
                     for (int j = 0; j < 4; ++j) {
                         // scale > 0: the shifted scores keep the order of the raw ones
                         st[qt][s][j] = __builtin_fmaf(st[qt][s][j], P.scale_log2, -m_ref[qt]);
-                        tmax = fmaxf(tmax, st[qt][s][j]);
+                        tmax[s] = fmaxf(tmax[s], st[qt][s][j]);
                     }
             }
-            if (__builtin_amdgcn_ballot_w64(unset || tmax > kLazyRescale) != 0) {
+#pragma unroll
+            for (int s = 1; s < N / 16; ++s)
+                tmax[0] = fmaxf(tmax[0], tmax[s]);
+            if (__builtin_amdgcn_ballot_w64(unset || tmax[0] > kLazyRescale) != 0) {
                 bool moved = false;
                 float alpha[QT];
 #pragma unroll
@@ -467,13 +589,12 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
             // i%4 of the 8 bytes addressed by lane 4e + i/4 as its element e, so
             // lane (c, g) addresses token 32kk + 16h + 4g + c/4, dims
             // 16nb + 4(c%4) .. +3, and receives 4 tokens of dim 16nb + c.
-            const _Float16* vsrc = &vs[(4 * g + c / 4) * VS + 4 * (c % 4)];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
                 for (int kk = 0; kk < N / 32; ++kk) {
-                    const s4 lo = ds_read_tr16(&vsrc[(32 * kk) * VS + 16 * nb]);
-                    const s4 hi = ds_read_tr16(&vsrc[(32 * kk + 16) * VS + 16 * nb]);
+                    const s4 lo = ds_read_tr16(&vs[32 * kk * D + voff[nb]]);
+                    const s4 hi = ds_read_tr16(&vs[(32 * kk + 16) * D + voff[nb]]);
                     const h8 va = __builtin_bit_cast(
                         h8, u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
                                   __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y});
@@ -484,6 +605,11 @@ __global__ __launch_bounds__(kMqThreads) void pa_mq_kernel(MqParams P)
                 }
             }
         }
+    };
+    for (int t0 = stream_begin; t0 < stream_end; t0 += 2 * N) {
+        step(t0, 0);
+        if (t0 + N < stream_end)
+            step(t0 + N, 1);
     }
 
     // ---- O^T[dim 16nb + 4g + j][query c] / l(query c) ----
