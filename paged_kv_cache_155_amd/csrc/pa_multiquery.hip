@@ -102,6 +102,18 @@ __device__ __forceinline__ s4 ds_read_tr16(const _Float16* p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
 }
 
+// The V^T operand of one MFMA (16 dims x 32 tokens): two transposing reads of
+// the tile's token rows 0..15 and 16..31 (rows of D halves) at this lane's
+// offset (elements).
+template <int D>
+__device__ __forceinline__ h8 read_vt(const _Float16* tile, int off)
+{
+    const s4 lo = ds_read_tr16(&tile[off]);
+    const s4 hi = ds_read_tr16(&tile[16 * D + off]);
+    return __builtin_bit_cast(h8, u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
+                                        __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y});
+}
+
 // max over the four 16-lane groups (lanes c, c+16, c+32, c+48)
 __device__ __forceinline__ float group_max(float x)
 {
@@ -576,6 +588,18 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
                     }
                 }
             }
+            // The V^T operands of the first kPreV dim blocks (token step 0) are read
+            // here, ahead of the exponentials they do not depend on, and the
+            // scheduling barrier keeps them here (the scheduler otherwise sinks
+            // every operand read to just before its products, where the wave then
+            // waits on it): 0.7% on the multi-query workload.
+            constexpr int kPreV = NB < 2 ? NB : 2;
+            h8 va_pre[kPreV];
+#pragma unroll
+            for (int nb = 0; nb < kPreV; ++nb)
+                va_pre[nb] = read_vt<D>(vs, voff[nb]);
+            __builtin_amdgcn_sched_barrier(0);
+
             // the weights, rounded to fp16 as P^T, the B operand of the next products
             h8 pb[QT][N / 32];
 #pragma unroll
@@ -605,11 +629,8 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
             for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
                 for (int kk = 0; kk < N / 32; ++kk) {
-                    const s4 lo = ds_read_tr16(&vs[32 * kk * D + voff[nb]]);
-                    const s4 hi = ds_read_tr16(&vs[(32 * kk + 16) * D + voff[nb]]);
-                    const h8 va = __builtin_bit_cast(
-                        h8, u32x4{__builtin_bit_cast(u32x2, lo).x, __builtin_bit_cast(u32x2, lo).y,
-                                  __builtin_bit_cast(u32x2, hi).x, __builtin_bit_cast(u32x2, hi).y});
+                    const h8 va = kk == 0 && nb < kPreV ? va_pre[nb < kPreV ? nb : 0]
+                                                        : read_vt<D>(vs + 32 * kk * D, voff[nb]);
 #pragma unroll
                     for (int qt = 0; qt < QT; ++qt)
                         o[qt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qt][kk], o[qt][nb],
