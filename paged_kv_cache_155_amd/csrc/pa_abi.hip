@@ -18,6 +18,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // of 256 threads fits.
 bool grid_fits(int64_t workgroups) { return workgroups <= (int64_t)(UINT32_MAX / 256); }
 
+// The kernels address a token row and a physical block of one cache with
+// 32-bit byte offsets: B * H * D * 2 (fp16) must fit.
+bool block_fits(int32_t block_size, int32_t num_heads, int32_t head_dim)
+{
+    return (int64_t)block_size * num_heads * head_dim * 2 <= INT32_MAX;
+}
+
 // Number of context partitions the grid covers, or -1 for bad arguments.
 int64_t num_partitions(int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size)
 {
@@ -131,7 +138,7 @@ int prepare_decode(pa::DecodeParams& p, void* out, const void* q, const void* k_
         return PA_ERR_INVALID_DIM;
     if (!supported_decode(head_dim, block_size))
         return PA_ERR_UNSUPPORTED;
-    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX || !block_fits(block_size, num_heads, head_dim))
         return PA_ERR_INVALID_DIM;
     if (partition_size < 0 || partition_size % block_size != 0)
         return PA_ERR_PARTITION;
@@ -419,7 +426,7 @@ int multi_query(void* out, const void* q, const void* k_cache, const void* v_cac
     if (!supported_decode(head_dim, block_size))
         return PA_ERR_UNSUPPORTED;
     if (!(std::isfinite(scale) && scale > 0.0f) ||
-        (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+        (int64_t)max_blocks_per_seq * block_size > INT32_MAX || !block_fits(block_size, num_heads, head_dim))
         return PA_ERR_INVALID_DIM;
     if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0)
         return PA_OK;

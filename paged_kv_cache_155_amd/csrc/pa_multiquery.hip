@@ -352,12 +352,18 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
     // will not make it a scalar one), issued before a chunk's direct loads and
     // made uniform only after the wait that lands them: taken earlier, it would
     // wait for every load issued before it.
-    auto wave_block = [&](int t0) { return table[min(t0 + WR * wave_u, stream_end - 1) / B]; };
+    // (positions and block ids are never negative: unsigned arithmetic is one
+    // shift and one 32 x 32 -> 64-bit product on the scalar unit)
+    auto wave_block = [&](int t0) {
+        return table[(uint32_t)min(t0 + WR * wave_u, stream_end - 1) / (uint32_t)B];
+    };
+    const uint32_t block_bytes = (uint32_t)block_elems * 2u;  // < 4 GiB: B * H * D * 2
     auto dma_chunk = [&](int t0, int b, int blk) {
         if (t0 + WR * wave_u >= stream_end)
             return;
-        const char* kb = k_bytes + (int64_t)blk * block_elems * 2;
-        const char* vb = v_bytes + (int64_t)blk * block_elems * 2;
+        const uint64_t off = (uint64_t)(uint32_t)blk * block_bytes;
+        const char* kb = k_bytes + off;
+        const char* vb = v_bytes + off;
 #pragma unroll
         for (int j = 0; j < DJ; ++j) {
             load_lds16(kb, &k_lds[b][(WR * wave_u + RPI * j) * D], dk[j]);

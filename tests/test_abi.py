@@ -78,6 +78,8 @@ def test_decode_rejects(lib):
     assert _decode(lib, S=0, out=P(0)) == 0          # nothing to do
     # 65536 x 256 workgroups of 256 threads would pass 2^32 work-items
     assert _decode(lib, S=65536, H=256) == -2
+    # a physical block of 32 x 2^19 heads x 128 fp16 values passes 2^31 bytes
+    assert _decode(lib, H=1 << 19, B=32) == -2
 
 
 def test_reshape_rejects(lib):
@@ -200,6 +202,8 @@ def test_multi_query_rejects(lib):
     assert _mq(lib, S=0, out=P(0)) == 0
     assert _mq(lib, T=0, out=P(0)) == 0
     assert _mq(lib, maxq=0, out=P(0)) == 0
+    # a physical block of 32 x 2^19 heads x 128 fp16 values passes 2^31 bytes
+    assert _mq(lib, H=1 << 19, B=32) == -2
 
 
 def _cascade_append(lib, **kw):
