@@ -49,7 +49,10 @@ extern "C" {
 enum {
     PA_OK = 0,
     PA_ERR_NULL = -1,        /* a required pointer is NULL                          */
-    PA_ERR_INVALID_DIM = -2, /* a size is <= 0 (num_tokens/num_seqs < 0) or overflows */
+    PA_ERR_INVALID_DIM = -2, /* a size is <= 0 (num_tokens/num_seqs < 0) or overflows:
+                                the grid, or (decode, cascade, multi-query) a physical
+                                block of block_size * num_heads * head_dim * 2 bytes
+                                past INT32_MAX                                        */
     PA_ERR_UNSUPPORTED = -3, /* head_dim or block_size not compiled in               */
     PA_ERR_PARTITION = -4,   /* partition_size not 0 and not a positive multiple of block_size */
     PA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than pa_decode_workspace_size */
