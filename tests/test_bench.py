@@ -9,7 +9,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_kernel_code_sha_does_not_depend_on_the_checkout_path(tmp_path):
     """roofline.traffic is matched to the device code by this hash; a copy
-    of the tree elsewhere (as on the GPU machine) must give the same value."""
+    of the tree at another path (another machine's checkout) must give the same
+    value."""
     for d in ("paged_kv_cache_155_amd", "include"):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
                         ignore=shutil.ignore_patterns("*.so", "__pycache__"))
