@@ -254,7 +254,9 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
     }
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
+    // the wave index is uniform: taken as a scalar, the row bounds and tests
+    // derived from it stay on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int g = lane / 16;  // lane group: owns dims [g*D/4, (g+1)*D/4) of K and Q
     const int c = lane % 16;  // this lane's query column of S^T (and token row of K)
 
@@ -313,10 +315,15 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
     // O^T, the row sums (every element of lsum[qt] holds the sum of query c), and
     // the reference the exponentials are taken against (scaled, base 2)
     f4 o[QT][NB], lsum[QT];
-    float m[QT];
+    // m: the reference (-inf until a row has a finite score); m_ref: the shift
+    // the scores take, m or 0 while m is unset; all_set (wave-uniform): no lane
+    // of the wave has an unset reference
+    float m[QT], m_ref[QT];
+    bool all_set = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         m[qt] = kNegInf;
+        m_ref[qt] = 0.0f;
         lsum[qt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -514,7 +521,7 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
 
             // positions at or past a row's limit: -inf (only in chunks that
             // cross some row's limit; a wave-uniform branch)
-            if (__builtin_amdgcn_readfirstlane((int)(t0 + N > wave_lo))) {
+            if (t0 + N > wave_lo) {
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) {
                     const int nvis = lim[qt] - t0 - 4 * g;  // visible offsets 16s + j < nvis
@@ -537,16 +544,12 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
             // or a reference is not yet set, are the row maxima formed and the
             // reference moved (the shift then corrected) -- the same decisions as
             // forming every chunk's max, at none of its cost in the usual chunk.
-            float m_ref[QT];
             float tmax[N / 16];  // partial maxima, independent chains
-            bool unset = false;
 #pragma unroll
             for (int s = 0; s < N / 16; ++s)
                 tmax[s] = kNegInf;
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) {
-                m_ref[qt] = m[qt] == kNegInf ? 0.0f : m[qt];
-                unset |= m[qt] == kNegInf;
 #pragma unroll
                 for (int s = 0; s < N / 16; ++s)
 #pragma unroll
@@ -559,8 +562,8 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int s = 1; s < N / 16; ++s)
                 tmax[0] = fmaxf(tmax[0], tmax[s]);
-            if (__builtin_amdgcn_ballot_w64(unset || tmax[0] > kLazyRescale) != 0) {
-                bool moved = false;
+            if (!all_set || __builtin_amdgcn_ballot_w64(tmax[0] > kLazyRescale) != 0) {
+                bool moved = false, unset = false;
                 float alpha[QT];
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) {
@@ -577,13 +580,16 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
                     alpha[qt] = up ? exp2_fast(m[qt] - ref_new) : 1.0f;
                     moved |= up;
                     m[qt] = m_new;
+                    unset |= m_new == kNegInf;
                     const float shift = ref_new - m_ref[qt];
+                    m_ref[qt] = ref_new;
 #pragma unroll
                     for (int s = 0; s < N / 16; ++s)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             st[qt][s][j] -= shift;
                 }
+                all_set = __builtin_amdgcn_ballot_w64(unset) == 0;
                 if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
                     for (int qt = 0; qt < QT; ++qt) {
