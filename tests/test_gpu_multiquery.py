@@ -69,6 +69,21 @@ def test_multi_query_chunked_prefill_batch(orc):
     log(f"[mq] max abs err {ea:.3e}")
 
 
+def test_multi_query_empty_chunks_and_loose_bound(orc):
+    """Sequences that bring no new rows (first, middle and last of the batch)
+    launch only tiles that return at once, and a max_query_len three times
+    the longest chunk only adds such tiles: every row that exists is written
+    (the output starts as NaN) and matches the oracle."""
+    from paged_kv_cache_155_amd.workloads import make_multi_query
+    ctx = [40, 300, 1, 129, 700, 64]
+    qn = [0, 37, 0, 129, 200, 0]
+    log("[mq] empty chunks, max_query_len 3x the longest chunk")
+    w, q, qs = make_multi_query(ctx, qn, 4, 128, 16, seed=21)
+    got, ref = _run_mq(orc, _live(w), q, qs, 3 * max(qn))
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "empty chunks")
+
+
 def test_multi_query_late_outlier_keys(orc):
     """Keys 30x larger at a few late positions (logit jumps of tens of log2
     units after the running maximum has settled), so the kernel moves its
