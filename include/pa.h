@@ -187,7 +187,10 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
  * so that the prefix is read once per 64 sequences and head (a workgroup
  * stages 64-token pieces of the prefix in LDS for the matrix-core products of
  * 64 queries) and each suffix once, all pieces merged with the log-sum-exp
- * identity.
+ * identity.  Each 128-token piece of the prefix leaves (max, sum, normalised
+ * row) per (sequence, head) in the workspace, the row rounded to fp16 (half
+ * the partial bytes; a relative error of at most 2^-11 per element before
+ * the merge, inside the decode's tolerance).
  *
  *   prefix_block_table  int32 [prefix_len / block_size], DEVICE: the prefix's
  *                       physical blocks in logical order
@@ -316,7 +319,8 @@ int pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_c
  * as in pa_decode_fp8 (k_scale, v_scale finite and > 0, else
  * PA_ERR_INVALID_DIM).  The prefix pass widens each staged code exactly to
  * fp16 for the matrix-core products; the K scale is folded into the logit
- * scale and the V scale into the rows.  prefix_len = 0 is pa_decode_fp8.
+ * scale and the V scale into the rows (for the prefix pieces' fp16 rows, when
+ * they are merged).  prefix_len = 0 is pa_decode_fp8.
  */
 int pa_decode_cascade_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* prefix_block_table, int32_t prefix_len,

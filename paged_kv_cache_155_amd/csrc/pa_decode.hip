@@ -267,6 +267,14 @@ __device__ __forceinline__ void merge_into(LaneState<KV>& st, float m_o, float l
     st.m = M;
 }
 
+// Element d of the row in workspace slot u written by the shared-prefix pass:
+// fp16 values at the start of the slot's row, without the FP8 V scale.
+template <int D>
+__device__ __forceinline__ float prefix_row(const DecodeParams& P, int64_t u, int d)
+{
+    return (float)reinterpret_cast<const _Float16*>(P.ws_o + u * D)[d] * P.v_scale;
+}
+
 // Column d of a row whose shared-prefix partials sit in workspace slots
 // 0 .. slot_base-1 of u0 and whose one suffix partition has (M, L, o):
 // the log-sum-exp merge, prefix slots first, then the suffix (L = 0: none).
@@ -281,7 +289,7 @@ __device__ float merge_with_prefix(const DecodeParams& P, int64_t u0, int d, flo
     for (int p = 0; p < P.slot_base; ++p) {
         const float w = P.ws_l[u0 + p] * exp2_fast(P.ws_m[u0 + p] - Mx);
         wsum += w;
-        acc = fmaf(w, P.ws_o[(u0 + p) * D + d], acc);
+        acc = fmaf(w, prefix_row<D>(P, u0 + p, d), acc);
     }
     if (L > 0.0f) {
         const float w = L * exp2_fast(M - Mx);
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
 // order p = 0, 1, ... (the weight broadcast from its lane with v_readlane),
 // up to sixteen slot loads in flight.
 // A fixed order, so the result is deterministic.
-template <int D>
+template <int D, bool kPrefix>
 __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
 {
     constexpr int CPL = D / kWave;  // output columns per lane
@@ -476,7 +484,11 @@ __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
         auto add = [&](int j) {
             const float wj = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-            if constexpr (CPL == 2) {
+            if (kPrefix && c0 + j < P.slot_base) {  // a shared-prefix slot (wave-uniform)
+#pragma unroll
+                for (int i = 0; i < CPL; ++i)
+                    acc[i] = fmaf(wj, prefix_row<D>(P, u0 + c0 + j, lane * CPL + i), acc[i]);
+            } else if constexpr (CPL == 2) {
                 const float2 o2 = *reinterpret_cast<const float2*>(oc + (int64_t)j * D);
                 acc[0] = fmaf(wj, o2.x, acc[0]);
                 acc[1] = fmaf(wj, o2.y, acc[1]);
@@ -543,10 +555,15 @@ hipError_t launch_decode_reduce(const DecodeParams& P, int head_dim, hipStream_t
     if (P.num_partitions <= 1)
         return hipSuccess;  // the partition kernel wrote every row
     const dim3 grid((uint32_t)(((int64_t)P.num_seqs * P.num_heads + kWaves - 1) / kWaves));
-    if (head_dim == 128)
-        hipLaunchKernelGGL((pa_reduce_kernel<128>), grid, dim3(kThreads), 0, stream, P);
+    // with shared-prefix slots (fp16 rows) in front of the partitions, or without
+    if (head_dim == 128 && P.slot_base > 0)
+        hipLaunchKernelGGL((pa_reduce_kernel<128, true>), grid, dim3(kThreads), 0, stream, P);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL((pa_reduce_kernel<128, false>), grid, dim3(kThreads), 0, stream, P);
+    else if (head_dim == 64 && P.slot_base > 0)
+        hipLaunchKernelGGL((pa_reduce_kernel<64, true>), grid, dim3(kThreads), 0, stream, P);
     else if (head_dim == 64)
-        hipLaunchKernelGGL((pa_reduce_kernel<64>), grid, dim3(kThreads), 0, stream, P);
+        hipLaunchKernelGGL((pa_reduce_kernel<64, false>), grid, dim3(kThreads), 0, stream, P);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -664,18 +664,30 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
         const int r = wr0 + 16 * qt + c;
         if (r >= n_rows)
             continue;
-        // FP8: the V scale (the K scale is in scale_log2)
-        const float inv = (l > 0.0f ? 1.0f / l : 0.0f) * (kFp8 ? P.v_scale : 1.0f);
         if constexpr (kCascade) {
+            // The normalised row in fp16, at the start of the slot's row (half
+            // the bytes of fp32 to write here and to read in the merge), without
+            // the FP8 V scale: the readers apply it, so the stored values stay
+            // within the cache's code range.
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
             const int64_t u = ((row0 + r) * P.num_heads + h) * P.num_slots + part;
+            _Float16* orow = reinterpret_cast<_Float16*>(P.ws_o + u * D);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                *reinterpret_cast<f4*>(&P.ws_o[u * D + nb * 16 + 4 * g]) = o[qt][nb] * inv;
+            for (int nb = 0; nb < NB; ++nb) {
+                typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+                h4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[j] = (_Float16)(o[qt][nb][j] * inv);
+                *reinterpret_cast<h4*>(&orow[nb * 16 + 4 * g]) = v;
+            }
             if (g == 0) {
                 P.ws_m[u] = m[qt];
                 P.ws_l[u] = l;
             }
         } else {
+            // FP8: the V scale (the K scale is in scale_log2)
+            const float inv = (l > 0.0f ? 1.0f / l : 0.0f) * (kFp8 ? P.v_scale : 1.0f);
             _Float16* orow = P.out + ((row0 + r) * P.num_heads + h) * D;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
