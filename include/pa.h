@@ -91,14 +91,17 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
 
 /*
  * Bytes of device workspace pa_decode needs for the split-context path:
- * fp32 partial results (output row, running maximum, running sum) for each
- * (sequence, head, context partition).  [src] §六 names a second version of
+ * partial results (normalised output row in fp16, running maximum and sum in
+ * fp32) for each (sequence, head, context partition).  [src] §六 names a second version of
  * PagedAttention ("v2") without describing it; the split reading here is
  * partitions of partition_size logical tokens starting at multiples of it,
  * each reduced to (max, sum, normalised row) and merged by the exact
- * log-sum-exp identity of the softmax in [10x] §2.1.  Layout in the
- * workspace: o [num_seqs, num_heads, NP, head_dim], then m and l
- * [num_seqs, num_heads, NP], each part starting at a 256-byte boundary,
+ * log-sum-exp identity of the softmax in [10x] §2.1 (the merge is exact in
+ * any precision of the rows; the fp16 rows, before any FP8 V scale, add at
+ * most 2^-11 relative per element, the size of the output's own rounding).
+ * Layout in the workspace: o [num_seqs, num_heads, NP, head_dim] fp16, then
+ * m and l [num_seqs, num_heads, NP] fp32, each part starting at a 256-byte
+ * boundary,
  * NP = ceil(max_blocks_per_seq * block_size / partition_size).  Returns 0
  * when no split happens (partition_size == 0, or a single partition covers
  * max_blocks_per_seq * block_size tokens) and 0 for invalid arguments (no
@@ -159,8 +162,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
  * call itself allocates and frees nothing.
  *   - A call whose pa_decode_workspace_size(...) exceeds
  *     PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_SCRATCH and enqueues nothing
- *     (32 MiB holds, e.g., 256 sequences x 40 heads x 4 partitions of
- *     head_dim 128: 21 MB).
+ *     (32 MiB holds, e.g., 256 sequences x 40 heads x 8 partitions of
+ *     head_dim 128: 21.6 MB).
  *   - The scratch is that of the calling thread's current device; `stream`
  *     must belong to that device.
  *   - Every call on a GPU shares that GPU's array, and nothing in it has to
@@ -188,9 +191,8 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
  * stages 64-token pieces of the prefix in LDS for the matrix-core products of
  * 64 queries) and each suffix once, all pieces merged with the log-sum-exp
  * identity.  Each 128-token piece of the prefix leaves (max, sum, normalised
- * row) per (sequence, head) in the workspace, the row rounded to fp16 (half
- * the partial bytes; a relative error of at most 2^-11 per element before
- * the merge, inside the decode's tolerance).
+ * row) per (sequence, head) in the workspace, the row in fp16 as pa_decode's
+ * partition rows.
  *
  *   prefix_block_table  int32 [prefix_len / block_size], DEVICE: the prefix's
  *                       physical blocks in logical order

@@ -47,7 +47,7 @@ WorkspaceLayout layout(int64_t units, int32_t head_dim)
 {
     auto round256 = [](size_t b) { return (b + 255) & ~size_t(255); };
     WorkspaceLayout w;
-    w.o_bytes = round256((size_t)units * head_dim * sizeof(float));
+    w.o_bytes = round256((size_t)units * head_dim * sizeof(_Float16));  // fp16 rows
     w.m_bytes = round256((size_t)units * sizeof(float));
     w.l_bytes = round256((size_t)units * sizeof(float));
     w.total = w.o_bytes + w.m_bytes + w.l_bytes;
@@ -185,7 +185,7 @@ int prepare_decode(pa::DecodeParams& p, void* out, const void* q, const void* k_
         if (!aligned16(workspace))
             return PA_ERR_ALIGN;
         char* base = static_cast<char*>(workspace);
-        p.ws_o = reinterpret_cast<float*>(base);
+        p.ws_o = reinterpret_cast<_Float16*>(base);
         p.ws_m = reinterpret_cast<float*>(base + w.o_bytes);
         p.ws_l = reinterpret_cast<float*>(base + w.o_bytes + w.m_bytes);
     }

@@ -267,12 +267,13 @@ __device__ __forceinline__ void merge_into(LaneState<KV>& st, float m_o, float l
     st.m = M;
 }
 
-// Element d of the row in workspace slot u written by the shared-prefix pass:
-// fp16 values at the start of the slot's row, without the FP8 V scale.
+// Element d of the partial row in workspace slot u (a partition's or a
+// shared-prefix piece's): stored in fp16 before the FP8 V scale, which is
+// applied here (v_scale = 1 for fp16 caches).
 template <int D>
-__device__ __forceinline__ float prefix_row(const DecodeParams& P, int64_t u, int d)
+__device__ __forceinline__ float slot_row(const DecodeParams& P, int64_t u, int d)
 {
-    return (float)reinterpret_cast<const _Float16*>(P.ws_o + u * D)[d] * P.v_scale;
+    return (float)P.ws_o[u * D + d] * P.v_scale;
 }
 
 // Column d of a row whose shared-prefix partials sit in workspace slots
@@ -289,7 +290,7 @@ __device__ float merge_with_prefix(const DecodeParams& P, int64_t u0, int d, flo
     for (int p = 0; p < P.slot_base; ++p) {
         const float w = P.ws_l[u0 + p] * exp2_fast(P.ws_m[u0 + p] - Mx);
         wsum += w;
-        acc = fmaf(w, prefix_row<D>(P, u0 + p, d), acc);
+        acc = fmaf(w, slot_row<D>(P, u0 + p, d), acc);
     }
     if (L > 0.0f) {
         const float w = L * exp2_fast(M - Mx);
@@ -417,16 +418,15 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
             o = fmaf(s_acc[w][d], wt, o);
         }
         o = o / L;
-        if constexpr (KV::kScaledOutput)
-            o *= P.v_scale;
+        const float o_scaled = KV::kScaledOutput ? o * P.v_scale : o;
         if (nparts_seq == 1 && P.slot_base == 0) {
-            P.out[row + d] = (_Float16)o;
+            P.out[row + d] = (_Float16)o_scaled;
         } else if (P.slot_base > 0 && P.num_partitions == 1) {
             P.out[row + d] = (_Float16)merge_with_prefix<D>(
-                P, ((int64_t)s * P.num_heads + h) * P.num_slots, d, M, L, o);
-        } else {
+                P, ((int64_t)s * P.num_heads + h) * P.num_slots, d, M, L, o_scaled);
+        } else {  // a partial row for the reduce: fp16, before the FP8 V scale
             const int64_t u = ((int64_t)s * P.num_heads + h) * P.num_slots + P.slot_base + part;
-            P.ws_o[u * D + d] = o;
+            P.ws_o[u * D + d] = (_Float16)o;
             if (d == 0) {
                 P.ws_m[u] = M;
                 P.ws_l[u] = L;
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
 // order p = 0, 1, ... (the weight broadcast from its lane with v_readlane),
 // up to sixteen slot loads in flight.
 // A fixed order, so the result is deterministic.
-template <int D, bool kPrefix>
+template <int D>
 __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
 {
     constexpr int CPL = D / kWave;  // output columns per lane
@@ -480,20 +480,16 @@ __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
             wsum += __shfl_xor(wsum, off);
         L += wsum;
         const int n = min(kWave, np - c0);
-        const float* oc = P.ws_o + (u0 + c0) * D + lane * CPL;
+        const _Float16* oc = P.ws_o + (u0 + c0) * D + lane * CPL;
         auto add = [&](int j) {
             const float wj = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-            if (kPrefix && c0 + j < P.slot_base) {  // a shared-prefix slot (wave-uniform)
-#pragma unroll
-                for (int i = 0; i < CPL; ++i)
-                    acc[i] = fmaf(wj, prefix_row<D>(P, u0 + c0 + j, lane * CPL + i), acc[i]);
-            } else if constexpr (CPL == 2) {
-                const float2 o2 = *reinterpret_cast<const float2*>(oc + (int64_t)j * D);
-                acc[0] = fmaf(wj, o2.x, acc[0]);
-                acc[1] = fmaf(wj, o2.y, acc[1]);
+            if constexpr (CPL == 2) {
+                const h2 o2 = *reinterpret_cast<const h2*>(oc + (int64_t)j * D);
+                acc[0] = fmaf(wj, (float)o2.x, acc[0]);
+                acc[1] = fmaf(wj, (float)o2.y, acc[1]);
             } else {
-                acc[0] = fmaf(wj, oc[(int64_t)j * D], acc[0]);
+                acc[0] = fmaf(wj, (float)oc[(int64_t)j * D], acc[0]);
             }
         };
         int j = 0;
@@ -513,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
     _Float16* orow = P.out + (int64_t)sh * D + lane * CPL;
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
-        orow[i] = (_Float16)(acc[i] / L);
+        orow[i] = (_Float16)(acc[i] / L * P.v_scale);  // the FP8 V scale (1 for fp16)
 }
 
 template <typename KV, int D, int B>
@@ -555,15 +551,10 @@ hipError_t launch_decode_reduce(const DecodeParams& P, int head_dim, hipStream_t
     if (P.num_partitions <= 1)
         return hipSuccess;  // the partition kernel wrote every row
     const dim3 grid((uint32_t)(((int64_t)P.num_seqs * P.num_heads + kWaves - 1) / kWaves));
-    // with shared-prefix slots (fp16 rows) in front of the partitions, or without
-    if (head_dim == 128 && P.slot_base > 0)
-        hipLaunchKernelGGL((pa_reduce_kernel<128, true>), grid, dim3(kThreads), 0, stream, P);
-    else if (head_dim == 128)
-        hipLaunchKernelGGL((pa_reduce_kernel<128, false>), grid, dim3(kThreads), 0, stream, P);
-    else if (head_dim == 64 && P.slot_base > 0)
-        hipLaunchKernelGGL((pa_reduce_kernel<64, true>), grid, dim3(kThreads), 0, stream, P);
+    if (head_dim == 128)
+        hipLaunchKernelGGL((pa_reduce_kernel<128>), grid, dim3(kThreads), 0, stream, P);
     else if (head_dim == 64)
-        hipLaunchKernelGGL((pa_reduce_kernel<64, false>), grid, dim3(kThreads), 0, stream, P);
+        hipLaunchKernelGGL((pa_reduce_kernel<64>), grid, dim3(kThreads), 0, stream, P);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -14,7 +14,7 @@ struct DecodeParams {
     const void* v_cache;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    float* ws_o;  // [S, H, NP, D] normalised partition rows (shared-prefix slots: fp16, see MqParams)
+    _Float16* ws_o;  // [S, H, NP, D] normalised partition rows in fp16, before any FP8 V scale
     float* ws_m;  // [S, H, NP] partition maxima (base-2 logits)
     float* ws_l;  // [S, H, NP] partition sums
     int32_t num_seqs;
@@ -38,9 +38,8 @@ constexpr int kCascadeTileRows = 64;  // shared-prefix sequences per workgroup
 
 struct MqParams {
     _Float16* out;                 // multi-query: final rows [T, H, D]
-    float* ws_o;                   // shared prefix: partials in slots 0..parts-1 of each (s, h);
-                                   // each row holds D fp16 values (without the FP8 V scale)
-                                   // at its start
+    _Float16* ws_o;                // shared prefix: partial rows (fp16, before any FP8 V scale)
+                                   // in slots 0..parts-1 of each (s, h)
     float* ws_m;
     float* ws_l;
     const _Float16* q;             // multi-query: [T, H, D]; shared prefix: [S, H, D]

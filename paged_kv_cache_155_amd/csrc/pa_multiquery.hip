@@ -665,13 +665,12 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
         if (r >= n_rows)
             continue;
         if constexpr (kCascade) {
-            // The normalised row in fp16, at the start of the slot's row (half
-            // the bytes of fp32 to write here and to read in the merge), without
-            // the FP8 V scale: the readers apply it, so the stored values stay
-            // within the cache's code range.
+            // The normalised row in fp16 (half the bytes of fp32 to write here
+            // and to read in the merge), without the FP8 V scale: the readers
+            // apply it, so the stored values stay within the cache's code range.
             const float inv = l > 0.0f ? 1.0f / l : 0.0f;
             const int64_t u = ((row0 + r) * P.num_heads + h) * P.num_slots + part;
-            _Float16* orow = reinterpret_cast<_Float16*>(P.ws_o + u * D);
+            _Float16* orow = P.ws_o + u * D;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 typedef _Float16 h4 __attribute__((ext_vector_type(4)));

@@ -45,7 +45,8 @@ def test_workspace_size(lib):
     assert pa.decode_workspace_size(8, 32, 128, 16, 32, 512) == 0  # one partition
     units = 8 * 32 * 64
     r = lambda b: (b + 255) // 256 * 256
-    assert pa.decode_workspace_size(8, 32, 128, 16, 2048, 512) == r(units * 512) + 2 * r(units * 4)
+    # fp16 rows (head_dim x 2 bytes), then fp32 maxima and sums
+    assert pa.decode_workspace_size(8, 32, 128, 16, 2048, 512) == r(units * 256) + 2 * r(units * 4)
     assert pa.decode_workspace_size(8, 32, 128, 16, 2048, 24) == 0  # invalid
 
 
@@ -140,11 +141,11 @@ def test_cascade_workspace_size(lib):
     # 512-token prefix in 128-token pieces (4 slots) + one suffix partition
     units = 8 * 32 * (4 + 1)
     assert pa.decode_cascade_workspace_size(8, 32, 128, 16, 512, 32, 0) == (
-        r(units * 128 * 4) + 2 * r(units * 4))
+        r(units * 128 * 2) + 2 * r(units * 4))
     # a prefix ending inside a piece still takes a slot; suffix split in 4
     units = 8 * 32 * (2 + 4)
     assert pa.decode_cascade_workspace_size(8, 32, 128, 16, 144, 128, 512) == (
-        r(units * 128 * 4) + 2 * r(units * 4))
+        r(units * 128 * 2) + 2 * r(units * 4))
     assert pa.decode_cascade_workspace_size(8, 32, 128, 16, -16, 32, 0) == 0
     assert pa.decode_cascade_workspace_size(8, 32, 128, 16, 512, 32, 24) == 0
 
