@@ -4,7 +4,8 @@ plain decode over the concatenated tables."""
 import numpy as np
 import pytest
 
-from gpu_util import DeviceWorkload, assert_close, log, oracle_after_write, to_dev
+from gpu_util import (DeviceWorkload, assert_close, assert_close_split_rows, log,
+                      oracle_after_write, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,6 +168,39 @@ def test_cascade_suffix_edges(orc, prefix_blocks, B, D):
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), ref, f"cascade edges P={P}")
 
+
+@pytest.mark.parametrize("P", [0, 16])
+def test_cascade_large_values(orc, P):
+    """|v| up to 60000 through the shared-prefix path: the prefix pieces'
+    rows are kept in fp16 (a normalised row lies within the range of V, so
+    nothing overflows; their rounding widens the tolerance as for the split
+    decode), P = 0 merges them in the partition kernel and P = 16 in the
+    reduce."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import make_random
+    log(f"[cascade] large values P={P}")
+    prefix_blocks, B, D = 9, 16, 128
+    suffix = [0, 1, 17, 300, 512, 40]
+    plen = prefix_blocks * B
+    w = make_random([plen + x for x in suffix], 2, D, B, seed=77, poison=True)
+    w.block_tables[:, :prefix_blocks] = w.block_tables[0, :prefix_blocks]
+    kc = w.k_cache.copy()
+    vc = (np.clip(w.v_cache.astype(np.float32), -5.0, 5.0) * 12000.0).astype(np.float16)
+    ok = w.slot_mapping >= 0  # the step's own slots hold poison until written: fill them
+    kc.reshape(-1, 2, D)[w.slot_mapping[ok]] = w.key[ok]
+    vc.reshape(-1, 2, D)[w.slot_mapping[ok]] = np.float16(-30000.0)
+    ref = orc.decode(w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale))
+    st = np.ascontiguousarray(w.block_tables[:, prefix_blocks:])
+    out = to_dev(np.full((len(suffix), 2, D), np.nan, dtype=np.float16))
+    pa.decode_cascade(out, to_dev(w.q), to_dev(kc), to_dev(vc),
+                      to_dev(w.block_tables[0, :prefix_blocks].astype(np.int32)), plen,
+                      to_dev(st), to_dev(np.array(suffix, dtype=np.int32)), float(w.scale),
+                      partition_size=P)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all() and np.abs(ref).max() > 1000.0
+    assert_close_split_rows(got, ref, 60000.0, f"cascade large values P={P}")
 
 @pytest.mark.parametrize("P", [0, 512])
 def test_cascade_needles_and_late_outliers_full(orc, P):
