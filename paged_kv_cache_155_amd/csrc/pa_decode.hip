@@ -41,7 +41,9 @@
 //   * base-2 exponent: logits are scaled by scale*log2(e) (times the K scale
 //     for FP8) and exponentiated with v_exp_f32;
 //   * split context: each partition writes (m, l, normalised row) to the
-//     workspace; the reduce kernel merges them with the log-sum-exp identity.
+//     workspace - the row in fp16 (half the bytes to write and read back; a
+//     normalised row lies within the range of V), m and l in fp32 - and the
+//     reduce kernel merges them with the log-sum-exp identity.
 //     A single-partition (sequence, head) writes its fp16 row directly - or,
 //     behind a shared prefix whose pieces already sit in the first workspace
 //     slots, merges those slots itself and writes the row.
@@ -441,7 +443,8 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
 // partitions i, i + 64, ...; M and sum_p w_p come from fixed butterflies; each
 // lane owns D / 64 output columns and adds w_p o_p over the partitions in
 // order p = 0, 1, ... (the weight broadcast from its lane with v_readlane),
-// up to sixteen slot loads in flight.
+// up to sixteen slot loads in flight; the rows are fp16 before any FP8 V
+// scale, which is applied once to the merged row.
 // A fixed order, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
