@@ -91,6 +91,41 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// Max over aligned groups of 16 lanes (the same DPP steps as group_sum).
+__device__ __forceinline__ float group_max16(float v)
+{
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    return fmaxf(v, dpp_mov<0x140>(v));
+}
+
+// Sum / max over the whole wave, every lane ending with the result: the
+// 16-lane groups by DPP, then the four groups by exchanging rows with
+// v_permlane32_swap and v_permlane16_swap (no LDS round trip).  Each step adds
+// a lane's value and its partner's, in either order: the same bits in both.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = group_sum<16>(v);
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = group_max16(v);
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int readlane(int v, int lane)
@@ -464,6 +499,58 @@ __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
     const int64_t u0 = (int64_t)sh * P.num_slots;
     const float* m = P.ws_m + u0;
     const float* l = P.ws_l + u0;
+    _Float16* orow = P.out + (int64_t)sh * D + lane * CPL;
+
+    constexpr int kFirst = 8;  // partitions the one-round-trip path takes
+    if (np <= kFirst) {
+        // The usual case, in one round trip after the context length: the
+        // (m, l) of partition `lane` and the rows of all np partitions are
+        // loaded together (the rows do not depend on the weights), and the
+        // wave's max and sum take register exchanges.  The rows are added in
+        // partition order, as in the general path below.
+        const bool has = lane < np;
+        const int lc = min(lane, np - 1);  // a written slot for every lane
+        const float m_raw = m[lc], l_raw = l[lc];
+        const _Float16* oc = P.ws_o + u0 * D + lane * CPL;
+        // Loads of rows past np read row np-1 again (a written slot) and go
+        // unused: straight-line loads, all in flight together (a load under
+        // a branch would be waited for before the branch joins).
+        float ob[kFirst][CPL];
+#pragma unroll
+        for (int j = 0; j < kFirst; ++j) {
+            const int64_t r = min(j, np - 1);
+            if constexpr (CPL == 2) {
+                const h2 o2 = *reinterpret_cast<const h2*>(oc + r * D);
+                ob[j][0] = (float)o2.x;
+                ob[j][1] = (float)o2.y;
+            } else {
+                ob[j][0] = (float)oc[r * D];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load above issued before the first wait
+        const float mp = has ? m_raw : kNegInf;
+        const float lp = has ? l_raw : 0.0f;
+        const float Mx = wave_max(mp);
+        const float w = has ? lp * exp2_fast(mp - Mx) : 0.0f;
+        const float Lx = wave_sum(w);
+        float acc[CPL] = {};
+        auto wj = [&](int j) {
+            return __builtin_bit_cast(float,
+                                      __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+        };
+#pragma unroll
+        for (int j = 0; j < kFirst; ++j) {
+            if (j < np) {
+#pragma unroll
+                for (int i = 0; i < CPL; ++i)
+                    acc[i] = fmaf(wj(j), ob[j][i], acc[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            orow[i] = (_Float16)(acc[i] / Lx * P.v_scale);  // the FP8 V scale (1 for fp16)
+        return;
+    }
 
     float M = kNegInf;
     for (int p = lane; p < np; p += kWave)
@@ -509,7 +596,6 @@ __global__ __launch_bounds__(kThreads) void pa_reduce_kernel(DecodeParams P)
         for (; j < n; ++j)
             add(j);
     }
-    _Float16* orow = P.out + (int64_t)sh * D + lane * CPL;
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
         orow[i] = (_Float16)(acc[i] / L * P.v_scale);  // the FP8 V scale (1 for fp16)
