@@ -43,9 +43,10 @@ struct WorkspaceLayout {
     size_t o_bytes, m_bytes, l_bytes, total;
 };
 
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
 WorkspaceLayout layout(int64_t units, int32_t head_dim)
 {
-    auto round256 = [](size_t b) { return (b + 255) & ~size_t(255); };
     WorkspaceLayout w;
     w.o_bytes = round256((size_t)units * head_dim * sizeof(_Float16));  // fp16 rows
     w.m_bytes = round256((size_t)units * sizeof(float));
@@ -201,6 +202,9 @@ constexpr int32_t kPrefixPartLen = 2 * pa::kMqChunk;  // shared-prefix tokens pe
 
 int32_t prefix_parts(int32_t prefix_len) { return (prefix_len + kPrefixPartLen - 1) / kPrefixPartLen; }
 
+// After the partials: the suffix launch's sequence order, ids then lengths
+size_t order_bytes(int32_t num_seqs) { return round256((size_t)num_seqs * 2 * sizeof(int32_t)); }
+
 }  // namespace
 
 size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
@@ -215,7 +219,7 @@ size_t pa_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_heads, int
                                         max_blocks_per_seq, partition_size);
     const int64_t slots =
         prefix_parts(prefix_len) + num_partitions(block_size, max_blocks_per_seq, partition_size);
-    return layout((int64_t)num_seqs * num_heads * slots, head_dim).total;
+    return layout((int64_t)num_seqs * num_heads * slots, head_dim).total + order_bytes(num_seqs);
 }
 
 namespace {
@@ -291,12 +295,19 @@ int cascade(void* out, const void* q, const void* key, const void* value, void* 
         return rc == 1 ? PA_OK : rc;
     if (!prefix_block_table)
         return PA_ERR_NULL;
+    const size_t partial_bytes =
+        layout((int64_t)num_seqs * num_heads * p.num_slots, head_dim).total;
+    if (workspace_bytes < partial_bytes + order_bytes(num_seqs))
+        return PA_ERR_WORKSPACE;
+    int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + partial_bytes);
+    p.seq_order = order;
+    p.seq_order_len = order + num_seqs;
     if (fp8) {  // the K scale folds into the logit scale, the V scale into the rows
         p.scale_log2 = (float)((double)scale * (double)fp8->k * 1.4426950408889634074);
         p.v_scale = fp8->v;
     }
     const int64_t row_tiles = ((int64_t)num_seqs + pa::kCascadeTileRows - 1) / pa::kCascadeTileRows;
-    if (row_tiles * num_heads * parts > INT32_MAX || !grid_fits(row_tiles * num_heads * parts))
+    if (row_tiles * num_heads * parts > INT32_MAX || !grid_fits(row_tiles * num_heads * parts + 1))
         return PA_ERR_INVALID_DIM;
     pa::MqParams m{};
     m.ws_o = p.ws_o;
@@ -316,6 +327,10 @@ int cascade(void* out, const void* q, const void* key, const void* value, void* 
     m.total_units = (uint32_t)(row_tiles * parts * num_heads);
     m.scale_log2 = p.scale_log2;
     m.v_scale = p.v_scale;
+    m.suffix_lens = context_lens;
+    m.order_max_len = max_blocks_per_seq * block_size;  // fits int32 (prepare_decode)
+    m.seq_order = order;
+    m.seq_order_len = order + num_seqs;
     if (append) {  // the prefix pass also writes the new tokens (into private suffix slots)
         m.new_k = static_cast<const _Float16*>(key);
         m.new_v = static_cast<const _Float16*>(value);
@@ -328,11 +343,12 @@ int cascade(void* out, const void* q, const void* key, const void* value, void* 
         m.slot_mapping = slot_mapping;
         m.cache_slots = (int64_t)num_blocks * block_size;
         const int64_t copy_units = pa::copy_workgroups(m, head_dim);
-        if (!grid_fits((int64_t)m.total_units + copy_units))
+        if (!grid_fits((int64_t)m.total_units + copy_units + 1))
             return PA_ERR_INVALID_DIM;
         m.copy_units = (uint32_t)copy_units;
     }
-    // Prefix pass first (slots 0..parts-1), then the suffix partitions; when
+    // Prefix pass first (slots 0..parts-1, and the order in which the suffix
+    // launch takes the sequences), then the suffix partitions; when
     // every suffix fits one partition the partition kernel merges the prefix
     // slots itself and writes the rows, else the reduce merges all slots.
     hipStream_t st = static_cast<hipStream_t>(stream);

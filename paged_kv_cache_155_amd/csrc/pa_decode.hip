@@ -21,7 +21,9 @@
 //     the hardware workgroup id is remapped so that each of the 8 XCDs (which
 //     receive workgroups round-robin) gets a contiguous range of that order:
 //     an XCD works through whole heads, and the long and short partitions of
-//     a ragged batch are spread evenly over time;
+//     a ragged batch are spread evenly over time.  After a shared-prefix pass
+//     the sequences are taken in the order that pass wrote, longest suffix
+//     first, so the launch ends on its shortest units;
 //   * K/V are streamed with nontemporal loads (read once, so they should not
 //     displace other lines in the caches);
 //   * every lane loads 16 bytes of a token's row of one head (8 fp16 or 16
@@ -347,12 +349,15 @@ __global__ __launch_bounds__(kThreads) void pa_partition_kernel(DecodeParams P)
     constexpr int EB = KV::kElemBytes;
 
     const uint32_t logical = xcd_remap(blockIdx.x, P.total_units);
-    const int s = (int)(logical % (uint32_t)P.num_seqs);
+    const uint32_t rank = logical % (uint32_t)P.num_seqs;
     const uint32_t rest = logical / (uint32_t)P.num_seqs;
     const int part = (int)(rest % (uint32_t)P.num_partitions);
     const int h = (int)(rest / (uint32_t)P.num_partitions);
-
-    const int ctx = P.context_lens[s];
+    // the rank-th sequence of the given order; its length is read by rank,
+    // so that both loads issue together
+    const int32_t* lens = P.seq_order != nullptr ? P.seq_order_len : P.context_lens;
+    const int ctx = lens[rank];
+    const int s = P.seq_order != nullptr ? P.seq_order[rank] : (int)rank;
     const int p0 = part * P.partition_size;
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;

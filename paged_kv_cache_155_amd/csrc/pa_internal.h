@@ -28,6 +28,11 @@ struct DecodeParams {
     int32_t slot_base;       // first workspace slot of partition 0 (1 when a shared-prefix
                              // partial occupies slot 0; partials are then always written)
     int32_t num_slots;       // workspace slots per (sequence, head) = slot_base + num_partitions
+    // shared-prefix decode: the order in which the workgroups take the
+    // sequences (ids by descending suffix length, and those lengths), written
+    // by the prefix pass; nullptr: sequence order, lengths from context_lens
+    const int32_t* seq_order;
+    const int32_t* seq_order_len;
 };
 
 // Several query rows against one K/V token stream (multi-query / shared prefix).
@@ -74,6 +79,12 @@ struct MqParams {
     const int64_t* slot_mapping;
     int64_t cache_slots;           // num_blocks * block_size
     float k_inv, v_inv;            // FP8: 1 / scale, rounded to float
+    // shared prefix: workgroup 0 orders the sequences for the suffix launch,
+    // by descending suffix_lens[s] clamped to [0, order_max_len]
+    const int32_t* suffix_lens;
+    int32_t order_max_len;         // max_blocks_per_seq * block_size of the suffix tables
+    int32_t* seq_order;            // [S] sequence ids
+    int32_t* seq_order_len;        // [S] their suffix_lens, as read
 };
 
 hipError_t launch_multiquery(const MqParams& p, int head_dim, int block_size, hipStream_t stream);

@@ -17,7 +17,9 @@
 //     prefix, which is therefore read once per tile of sequences instead of
 //     once per sequence.  The prefix is cut into partitions so that the short
 //     stream still fills the chip; each yields a log-sum-exp partial that the
-//     decode reduce merges with the partials of the private suffixes.
+//     decode reduce merges with the partials of the private suffixes.  One
+//     more workgroup of this launch orders the sequences by suffix length for
+//     the suffix launch that follows (longest first).
 //
 // Per chunk of the stream (32 tokens for fp16 multi-query, 64 otherwise):
 //   * the workgroup loads it once into LDS, [token][dim] tiles with unpadded
@@ -60,6 +62,7 @@ constexpr int kWaves = kMqThreads / kWave;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLazyRescale = 8.0f;  // log2 units: weights stay below 256
 constexpr int kCopyItems = 4;         // new-row pieces per thread of a copy workgroup
+constexpr int kOrderBuckets = 1024;   // suffix-length buckets of the ordering workgroup
 // s_waitcnt vmcnt(0), the other counters left alone (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -213,6 +216,65 @@ __device__ void copy_new_rows(const MqParams& P, uint32_t wg)
     }
 }
 
+// Shared-prefix pass, workgroup 0: the order in which the suffix launch that
+// follows takes the sequences, longest suffix first, so that its long units
+// start early and the launch drains on short ones.  A counting sort on the
+// suffix length (descending; clamped to [0, order_max_len] and grouped into at
+// most kOrderBuckets buckets of equal width): histogram, exclusive scan,
+// scatter, with LDS atomics.  Sequences of one bucket come in whatever order
+// the atomics give; the order decides only which workgroup computes which
+// sequence, never a result.  cnt: kOrderBuckets + kWaves ints of LDS.
+__device__ void order_by_suffix_length(const MqParams& P, int* cnt)
+{
+    constexpr int kPer = kOrderBuckets / kMqThreads;  // buckets per thread in the scan
+    static_assert(kOrderBuckets % kMqThreads == 0, "scan geometry");
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int max_len = P.order_max_len;
+    const int width = max_len / kOrderBuckets + 1;  // (max_len - 0) / width < kOrderBuckets
+    auto bucket = [&](int len) { return (max_len - min(max(len, 0), max_len)) / width; };
+
+    for (int b = tid; b < kOrderBuckets; b += kMqThreads)
+        cnt[b] = 0;
+    __syncthreads();
+    for (int i = tid; i < P.num_seqs; i += kMqThreads)
+        atomicAdd(&cnt[bucket(P.suffix_lens[i])], 1);
+    __syncthreads();
+    // exclusive scan: thread t owns buckets [kPer t, kPer t + kPer)
+    int c[kPer], own = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        c[j] = cnt[kPer * tid + j];
+        own += c[j];
+    }
+    int incl = own;  // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d)
+            incl += y;
+    }
+    if (lane == kWave - 1)
+        cnt[kOrderBuckets + wave] = incl;
+    __syncthreads();
+    int start = incl - own;
+    for (int w = 0; w < wave; ++w)
+        start += cnt[kOrderBuckets + w];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {  // this thread's buckets only
+        cnt[kPer * tid + j] = start;
+        start += c[j];
+    }
+    __syncthreads();
+    for (int i = tid; i < P.num_seqs; i += kMqThreads) {
+        const int len = P.suffix_lens[i];
+        const int pos = atomicAdd(&cnt[bucket(len)], 1);
+        if (pos < P.num_seqs) {  // always, unless the lengths changed between the reads
+            P.seq_order[pos] = i;
+            P.seq_order_len[pos] = len;
+        }
+    }
+}
+
 // Chunk length and the waves per SIMD asked of the compiler.  The fp16
 // multi-query tile takes 32-token chunks: half the score and weight registers
 // and half the LDS of 64, so that three workgroups (three waves per SIMD) fit
@@ -246,11 +308,19 @@ __global__ __launch_bounds__(kMqThreads) __attribute__((amdgpu_waves_per_eu(
 
     uint32_t wg = blockIdx.x;
     if constexpr (kCascade) {
+        static_assert(N * D * sizeof(_Float16) >= (kOrderBuckets + kWaves) * sizeof(int),
+                      "the ordering workgroup's counters fit in one K tile");
+        if (wg == P.copy_units + P.total_units) {  // the ordering workgroup, last
+            order_by_suffix_length(P, reinterpret_cast<int*>(&k_lds[0][0]));
+            return;
+        }
         if (wg < P.copy_units) {  // a copy workgroup (appending form only)
             copy_new_rows<D, kFp8>(P, wg);
             return;  // the whole workgroup, before any barrier
         }
-        wg -= P.copy_units;  // a multiple of 8: the XCD of each prefix unit is kept
+        // A multiple of 8: each prefix unit stays on the XCD whose suffix
+        // workgroups (same heads) merge its slots, from that XCD's L2.
+        wg -= P.copy_units;
     }
 
     const int tid = threadIdx.x;
@@ -705,7 +775,8 @@ template <bool kCascade, bool kFp8>
 hipError_t launch_mq(const MqParams& P, int head_dim, int block_size, hipStream_t stream)
 {
     constexpr int QT = (kCascade ? kCascadeTileRows : kMqTileRows) / (kWaves * 16);
-    const dim3 grid(P.total_units + (kCascade ? P.copy_units : 0u)), block(kMqThreads);
+    // shared prefix: the copy workgroups, the prefix units, the ordering workgroup
+    const dim3 grid(P.total_units + (kCascade ? 1u + P.copy_units : 0u)), block(kMqThreads);
     if (head_dim == 128 && block_size == 16)
         hipLaunchKernelGGL((pa_mq_kernel<128, 16, kCascade, QT, kFp8>), grid, block, 0, stream, P);
     else if (head_dim == 128 && block_size == 32)

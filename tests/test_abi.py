@@ -138,14 +138,18 @@ def test_cascade_workspace_size(lib):
     # no prefix: the plain decode's workspace
     assert (pa.decode_cascade_workspace_size(8, 32, 128, 16, 0, 128, 512)
             == pa.decode_workspace_size(8, 32, 128, 16, 128, 512))
-    # 512-token prefix in 128-token pieces (4 slots) + one suffix partition
+    # 512-token prefix in 128-token pieces (4 slots) + one suffix partition;
+    # then the suffix order (8 ids and 8 lengths)
     units = 8 * 32 * (4 + 1)
     assert pa.decode_cascade_workspace_size(8, 32, 128, 16, 512, 32, 0) == (
-        r(units * 128 * 2) + 2 * r(units * 4))
+        r(units * 128 * 2) + 2 * r(units * 4) + r(8 * 2 * 4))
     # a prefix ending inside a piece still takes a slot; suffix split in 4
     units = 8 * 32 * (2 + 4)
     assert pa.decode_cascade_workspace_size(8, 32, 128, 16, 144, 128, 512) == (
-        r(units * 128 * 2) + 2 * r(units * 4))
+        r(units * 128 * 2) + 2 * r(units * 4) + r(8 * 2 * 4))
+    units = 300 * 8 * (1 + 1)
+    assert pa.decode_cascade_workspace_size(300, 8, 64, 16, 64, 32, 0) == (
+        r(units * 64 * 2) + 2 * r(units * 4) + r(300 * 2 * 4))
     assert pa.decode_cascade_workspace_size(8, 32, 128, 16, -16, 32, 0) == 0
     assert pa.decode_cascade_workspace_size(8, 32, 128, 16, 512, 32, 24) == 0
 

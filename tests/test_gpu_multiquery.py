@@ -281,6 +281,65 @@ def test_cascade_repeated_calls_and_determinism(orc):
         "cascade not bitwise deterministic across calls"
 
 
+@pytest.mark.parametrize("max_suffix", [600, 1100], ids=["exact_order", "bucketed_order"])
+def test_cascade_suffix_order(orc, max_suffix):
+    """The prefix pass orders the sequences for the suffix launch (longest
+    suffix first).  300 sequences (more than one per thread of the ordering
+    workgroup), ties, empty suffixes and the longest possible one: the
+    result is the oracle's; the order written after the partials is a
+    permutation whose lengths do not increase (exactly when the suffix tables
+    cover fewer than 1024 tokens, by buckets of 2 tokens at 1100); and the
+    batch with its sequences reversed on the host gives the same rows
+    bitwise."""
+    import torch
+    import paged_kv_cache_155_amd as pa
+    from paged_kv_cache_155_amd.workloads import make_random
+    S, H, D, B, prefix_blocks = 300, 2, 128, 16, 4
+    rng = np.random.default_rng(max_suffix)
+    suffix = rng.integers(0, max_suffix + 1, S)
+    suffix[:40] = rng.choice([0, 1, 17, 17, 256], 40)  # ties and empty suffixes
+    suffix[57] = suffix[58] = max_suffix
+    plen = prefix_blocks * B
+    log(f"[cascade] suffix order S={S} max suffix {max_suffix}")
+    w = make_random([plen + int(x) for x in suffix], H, D, B, seed=max_suffix, poison=True)
+    w.block_tables[:, :prefix_blocks] = w.block_tables[0, :prefix_blocks]
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    ok = w.slot_mapping >= 0
+    kc.reshape(-1, H, D)[w.slot_mapping[ok]] = np.float16(0.1)   # no new token here
+    vc.reshape(-1, H, D)[w.slot_mapping[ok]] = np.float16(0.2)
+    ref = orc.decode(w.q, kc, vc, w.block_tables, w.context_lens, float(w.scale))
+    prefix = w.block_tables[0, :prefix_blocks].astype(np.int32)
+    st = np.ascontiguousarray(w.block_tables[:, prefix_blocks:])
+    max_len = st.shape[1] * B
+    assert (max_len < 1024) == (max_suffix < 1024)
+    sl = suffix.astype(np.int32)
+    need = pa.decode_cascade_workspace_size(S, H, D, B, plen, st.shape[1], 0)
+    dk, dv, dp = to_dev(kc), to_dev(vc), to_dev(prefix)
+
+    def run(q, tables, lens):
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        out = to_dev(np.full((S, H, D), np.nan, dtype=np.float16))
+        pa.decode_cascade(out, to_dev(q), dk, dv, dp, plen, to_dev(tables), to_dev(lens),
+                          float(w.scale), partition_size=0, workspace=ws)
+        torch.cuda.synchronize()
+        order = ws[need - (S * 8 + 255) // 256 * 256:].cpu().numpy()[:S * 8].view(np.int32)
+        return out.cpu().numpy(), order[:S], order[S:]
+
+    got, ids, lens = run(w.q, st, sl)
+    assert_close(got, ref, "cascade, ordered suffixes")
+    assert sorted(ids.tolist()) == list(range(S)), "the order is not a permutation"
+    assert np.array_equal(lens, sl[ids]), "the order's lengths are not the sequences' lengths"
+    width = max_len // 1024 + 1
+    keys = (max_len - lens) // width
+    assert np.all(np.diff(keys) >= 0), "suffix lengths increase along the order"
+    if width == 1:
+        assert np.all(np.diff(lens) <= 0)
+    rev = np.arange(S)[::-1]
+    got_rev, _, _ = run(w.q[rev], st[rev], sl[rev])
+    assert np.array_equal(got_rev[rev].view(np.uint16), got.view(np.uint16)), \
+        "a sequence's rows depend on the batch order"
+
+
 def test_multi_query_bench_workload_sampled(orc):
     """The launch bench.py --op multi_query times (16 sequences of 2048
     positions, the last 512 new, 32 heads x 128, B = 16, the same seeded
