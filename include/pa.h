@@ -192,10 +192,11 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
  * 64 queries) and each suffix once, all pieces merged with the log-sum-exp
  * identity.  Each 128-token piece of the prefix leaves (max, sum, normalised
  * row) per (sequence, head) in the workspace, the row in fp16 as pa_decode's
- * partition rows.  The same launch writes, in the workspace's last
- * round_up(8 * num_seqs, 256) bytes, the order in which the suffix launch
- * takes the sequences: num_seqs int32 ids by descending suffix length, then
- * their lengths (a schedule only: every order gives the same bits).
+ * partition rows.  The same launch writes, in the last round_up(8 * num_seqs,
+ * 256) bytes of the pa_decode_cascade_workspace_size(...) it needs, the order
+ * in which the suffix launch takes the sequences: num_seqs int32 ids by
+ * descending suffix length, then their lengths (a schedule only: every order
+ * gives the same bits).
  *
  *   prefix_block_table  int32 [prefix_len / block_size], DEVICE: the prefix's
  *                       physical blocks in logical order
