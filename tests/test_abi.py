@@ -174,6 +174,9 @@ def test_cascade_rejects(lib):
     assert _cascade(lib, B=8, plen=64) == -3
     assert _cascade(lib, P=24) == -4
     assert _cascade(lib, wsb=16) == -5               # prefix slots need a workspace
+    need = lib.pa_decode_cascade_workspace_size(2, 4, 128, 16, 64, 4, 0)
+    assert _cascade(lib, wsb=need - 256) == -5       # the partials fit, the sequence order not
+    assert _cascade(lib, wsb=need - 1) == -5
     assert _cascade(lib, q=P(0x10008)) == -6
     assert _cascade(lib, out=P(0)) == -1
     assert _cascade(lib, pt=P(0)) == -1              # checked after the decode arguments
